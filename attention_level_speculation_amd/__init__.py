@@ -1,0 +1,18 @@
+"""Speculative flash-decode step of attention-level speculation (ALSpec) on
+AMD Instinct MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind the C ABI of
+include/alspec.h (libalspec.so, built in-tree); this package is the thin
+Python binding over it.  Importing fails if the library is not built.
+"""
+from ._binding import (AlspecError, Events, Handle, KV_BF16, KV_F32,
+                       LIB_PATH, Params, alloc_outputs, alloc_workspace,
+                       flash_decode_exact, lse_combine, make_params,
+                       params_for, plan_splits, sink_approx, spec_decode,
+                       status_string, verify, version, workspace_size)
+
+__all__ = ["AlspecError", "Events", "Handle", "KV_BF16", "KV_F32",
+           "LIB_PATH", "Params", "alloc_outputs", "alloc_workspace",
+           "flash_decode_exact", "lse_combine", "make_params", "params_for",
+           "plan_splits", "sink_approx", "spec_decode", "status_string",
+           "verify", "version", "workspace_size"]

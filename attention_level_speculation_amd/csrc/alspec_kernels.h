@@ -1,0 +1,49 @@
+// Launchers of the gfx950 kernels (host functions defined in
+// alspec_kernels.hip).  Each enqueues its kernel(s) on `s` and returns the
+// HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "alspec_plan.h"
+
+namespace alspec {
+
+struct WsPtrs {
+  unsigned *counters;
+  float2 *part_ml;   // [slots][Hq] (m, l), m in log2 units
+  float *part_acc;   // [slots][Hq][D]
+  float2 *stA_ml;    // [B][Hq] merged sink+window state
+  float *stA_acc;    // [B][Hq][D]
+  float2 *headnd;    // [B][Hq] per-head (num, den) of the verify
+};
+
+WsPtrs ws_ptrs(void *ws, const Workspace &wl);
+
+// Split states over the sink and window splits (approx_set = true) or the
+// middle splits (false).  With `combine`, the last block of each
+// (entry, kv head) merges its sink+window states into o_approx, lse_approx
+// (may be null) and the merged state in the workspace.
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
+                           bool combine, const float *q, const void *k,
+                           const void *v, float sm_log2, const WsPtrs &w,
+                           float *o_approx, float *lse_approx, hipStream_t s);
+
+// Exact merge of the stored sink+window state with the middle splits, then
+// the relative L2 verify, the commit flag and the committed output.
+hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
+                               const float *o_approx, float *o_exact,
+                               float *lse_exact, float *ratio, uint8_t *commit,
+                               float *o_committed, float lambda,
+                               hipStream_t s);
+
+// Exact merge of every split state of the plan.
+hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
+                              float *o_exact, float *lse_exact, hipStream_t s);
+
+// Standalone verify of two output buffers.
+hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,
+                         const float *o_exact, float *ratio, uint8_t *commit,
+                         float *o_committed, float lambda, hipStream_t s);
+
+}  // namespace alspec

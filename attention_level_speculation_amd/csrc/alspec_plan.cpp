@@ -1,0 +1,127 @@
+// Split plan: validation of the parameters, the sink / window / middle sets
+// of every batch entry, their split into work items, and the workspace
+// layout.  Host C++ only.
+#include "alspec_plan.h"
+
+#include <math.h>
+#include <string.h>
+
+namespace alspec {
+
+namespace {
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int pow2_floor(int x) {
+  int r = 1;
+  while (r * 2 <= x) r *= 2;
+  return r;
+}
+
+}  // namespace
+
+alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
+  if (!p || !pa || !ws) return ALSPEC_ERR_INVALID_ARG;
+  const int B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  const int D = p->head_dim;
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || p->kv_capacity < 1)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ALSPEC_ERR_INVALID_ARG;
+  if (!p->seq_lens) return ALSPEC_ERR_INVALID_ARG;
+  if (p->sink < 0 || p->window < 0 ||
+      (int64_t)p->sink + (int64_t)p->window < 1)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (!(p->sm_scale > 0.f) || isinf(p->sm_scale)) return ALSPEC_ERR_INVALID_ARG;
+  if (!(p->lambda >= 0.f)) return ALSPEC_ERR_INVALID_ARG;  // NaN, negative
+  if (p->kv_dtype != ALSPEC_KV_F32 && p->kv_dtype != ALSPEC_KV_BF16)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (p->split_tokens < 0 || p->window_split_tokens < 0)
+    return ALSPEC_ERR_INVALID_ARG;
+  for (int b = 0; b < B && b < kMaxBatch; ++b)
+    if (p->seq_lens[b] < 1 || p->seq_lens[b] > p->kv_capacity)
+      return ALSPEC_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  if (B > kMaxBatch || Hkv > kMaxKvHeads) return ALSPEC_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ALSPEC_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ALSPEC_ERR_UNSUPPORTED;
+
+  memset(pa, 0, sizeof *pa);
+  pa->B = B;
+  pa->Hq = Hq;
+  pa->Hkv = Hkv;
+  pa->G = G;
+  pa->D = D;
+  pa->L_cap = p->kv_capacity;
+
+  // Sets of every entry.
+  int64_t mid_tokens = 0;
+  int max_win = 0;
+  for (int b = 0; b < B; ++b) {
+    const int L = p->seq_lens[b];
+    const int s_end = p->sink < L ? p->sink : L;
+    int64_t wb = (int64_t)L - (int64_t)p->window;
+    if (wb < s_end) wb = s_end;
+    pa->L[b] = L;
+    pa->s_end[b] = s_end;
+    pa->w_begin[b] = (int)wb;
+    mid_tokens += ((int)wb - s_end) * (int64_t)Hkv;
+    if (L - (int)wb > max_win) max_win = L - (int)wb;
+  }
+
+  // Middle split length: enough work items to cover the CUs several times
+  // over, but splits long enough that the per-split state stays a small
+  // share of the bytes read.
+  int T = p->split_tokens;
+  if (T == 0) {
+    const int64_t target_items = (int64_t)4 * kNominalCUs;
+    int64_t t = mid_tokens / (target_items > 0 ? target_items : 1);
+    if (t < 256) t = 256;
+    if (t > 4096) t = 4096;
+    T = pow2_floor((int)t);
+  }
+  // Window split length: the window is on the approximation's latency path,
+  // so it is cut finer (about 16 splits for a window of 2048).
+  int Tw = p->window_split_tokens;
+  if (Tw == 0) {
+    Tw = max_win / 16;
+    if (Tw < 64) Tw = 64;
+    if (Tw > 512) Tw = 512;
+    Tw = pow2_floor(Tw);
+  }
+  pa->T = T;
+  pa->Tw = Tw;
+
+  int slots = 0;
+  pa->itemA_pre[0] = 0;
+  pa->itemM_pre[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const int L = pa->L[b], s_end = pa->s_end[b], wb = pa->w_begin[b];
+    pa->nsink[b] = s_end > 0 ? 1 : 0;
+    pa->nwin[b] = ceil_div(L - wb, Tw);
+    pa->nmid[b] = ceil_div(wb - s_end, T);
+    pa->slot_base[b] = slots;
+    slots += pa->nsink[b] + pa->nwin[b] + pa->nmid[b];
+    pa->itemA_pre[b + 1] =
+        pa->itemA_pre[b] + (pa->nsink[b] + pa->nwin[b]) * Hkv;
+    pa->itemM_pre[b + 1] = pa->itemM_pre[b] + pa->nmid[b] * Hkv;
+  }
+  pa->total_slots = slots;
+
+  size_t off = 0;
+  ws->off_counters = off;
+  off += kCounterBytes;
+  ws->off_part_ml = off;
+  off = align_up(off + (size_t)slots * Hq * 8, kWsAlign);
+  ws->off_part_acc = off;
+  off = align_up(off + (size_t)slots * Hq * D * 4, kWsAlign);
+  ws->off_stA_ml = off;
+  off = align_up(off + (size_t)B * Hq * 8, kWsAlign);
+  ws->off_stA_acc = off;
+  off = align_up(off + (size_t)B * Hq * D * 4, kWsAlign);
+  ws->off_headnd = off;
+  off = align_up(off + (size_t)B * Hq * 8, kWsAlign);
+  ws->total = off;
+  return ALSPEC_OK;
+}
+
+}  // namespace alspec

@@ -1,0 +1,58 @@
+// Split plan and workspace layout of the speculative flash-decode step.
+// Host-side C++ shared by the C ABI and the kernel launchers.  Holds no GPU
+// code.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "alspec.h"
+
+namespace alspec {
+
+constexpr int kMaxBatch = ALSPEC_MAX_BATCH;
+constexpr int kMaxKvHeads = ALSPEC_MAX_KV_HEADS;
+constexpr size_t kWsAlign = 256;
+// counters at the start of every workspace, independent of the shape, so a
+// workspace reused for another shape still finds them at zero:
+//   [0, kMaxBatch*kMaxKvHeads)          approximation merge, per (b, g)
+//   [kApproxCounters, + kMaxBatch)      verify, per b
+constexpr int kApproxCounters = kMaxBatch * kMaxKvHeads;
+constexpr int kNumCounters = kApproxCounters + kMaxBatch;
+constexpr size_t kCounterBytes = 32768;
+static_assert(kNumCounters * 4 <= (int)kCounterBytes, "counter region");
+
+// Everything a kernel needs to map a block index to its work; passed by
+// value as a kernel argument.
+struct PlanArgs {
+  int B, Hq, Hkv, G, D, L_cap;
+  int T;   // middle split length (tokens)
+  int Tw;  // window split length (tokens)
+  int total_slots;
+  int L[kMaxBatch];
+  int s_end[kMaxBatch];    // sink = [0, s_end)
+  int w_begin[kMaxBatch];  // window = [w_begin, L), middle = [s_end, w_begin)
+  int nsink[kMaxBatch];    // 0 or 1 sink split
+  int nwin[kMaxBatch];     // window splits
+  int nmid[kMaxBatch];     // middle splits
+  int slot_base[kMaxBatch];       // first slot of user b: sink, window, middle
+  int itemA_pre[kMaxBatch + 1];   // prefix of (nsink + nwin) * Hkv
+  int itemM_pre[kMaxBatch + 1];   // prefix of nmid * Hkv
+};
+
+struct Workspace {
+  size_t off_counters, off_part_ml, off_part_acc, off_stA_ml, off_stA_acc,
+      off_headnd, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Nominal compute-unit count of an MI355X; the automatic split length aims
+// at a few work items per CU.  The plan depends on the parameters only, so
+// the workspace size needs no device.
+constexpr int kNominalCUs = 256;
+
+// Validate `p` and fill the plan.  Returns ALSPEC_OK or the status to report.
+alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws);
+
+}  // namespace alspec

@@ -1,0 +1,210 @@
+/*
+ * alspec.h -- C ABI of the speculative flash-decode step of attention-level
+ * speculation (ALSpec) on AMD Instinct MI355X (gfx950).
+ *
+ * The method, as the pages state it ("Attention-Level Speculation",
+ * atlas.scime.ai summary, sections Summary and Approach; ICML 2025 poster
+ * page, abstract): each layer's self-attention output is speculated with a
+ * cheap attention-sink approximation, exact attention is computed while the
+ * work after attention proceeds on the approximation, and the approximation
+ * is then verified with a relative L2 threshold (lambda = 0.10 in the
+ * evaluation, Key results) and committed or discarded.  The pages name a
+ * speculative flash-decode kernel and flash decoding as its basis; this
+ * library is a new gfx950 design of that step for one decode token.
+ *
+ * Notation.  B batch entries (one user's token through one layer each), Hq
+ * query heads, Hkv kv heads, G = Hq / Hkv query heads per kv head (query
+ * head h reads kv head h / G), head dimension D, per-entry context length
+ * L_b <= L_cap.  With S' = min(S, L_b):
+ *   sink   = tokens [0, S'),
+ *   window = tokens [max(S', L_b - W), L_b),
+ *   middle = tokens [S', max(S', L_b - W)).
+ * The approximation is softmax attention over sink + window, renormalised
+ * over that set; exact attention covers [0, L_b).  Logits are
+ * sm_scale * <q, k>.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless marked "host".  Layouts are dense
+ *    row-major with the last index fastest:
+ *      q, o_*        : float32 [B][Hq][D]
+ *      k, v          : [B][Hkv][L_cap][D] of the kv dtype (float32, or bf16
+ *                      stored as 16-bit patterns), 16-byte aligned
+ *      lse_*         : float32 [B][Hq] (natural log of the softmax
+ *                      normaliser, logits included)
+ *      ratio         : float32 [B];  commit : uint8 [B] (1 = commit)
+ *  - The caller owns every buffer and stream.  The library allocates no
+ *    device memory and keeps no pointer after a call returns.
+ *  - Compute calls only enqueue work on the given stream(s); they do not
+ *    synchronise.  Arguments are validated on the host first; on any
+ *    validation failure nothing is enqueued and a status other than
+ *    ALSPEC_OK is returned.  A HIP launch error is reported as
+ *    ALSPEC_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Streams are hipStream_t values passed as void* (NULL = the legacy
+ *    default stream); events are hipEvent_t passed as void*.
+ *  - Workspace: size from alspec_workspace_size.  A new workspace must be
+ *    zero-filled once before its first use; every call leaves the
+ *    workspace's internal counters at zero again when its work completes.
+ *    Calls whose work may overlap in time must not share a workspace.
+ *    The pointer must be 256-byte aligned.
+ *  - Handles: one handle may be used by one host thread at a time.
+ */
+#ifndef ALSPEC_H
+#define ALSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ALSPEC_OK = 0,
+  ALSPEC_ERR_INVALID_ARG = 1, /* null pointer, bad size, out-of-range value */
+  ALSPEC_ERR_UNSUPPORTED = 2, /* valid but outside the built shapes */
+  ALSPEC_ERR_WORKSPACE = 3,   /* workspace too small or misaligned */
+  ALSPEC_ERR_HIP = 4          /* the HIP runtime reported an error */
+} alspec_status;
+
+typedef enum { ALSPEC_KV_F32 = 0, ALSPEC_KV_BF16 = 1 } alspec_kv_dtype;
+
+/* Shape and method parameters of one call (all fields host values). */
+typedef struct {
+  int32_t batch;        /* B, 1 .. ALSPEC_MAX_BATCH */
+  int32_t num_q_heads;  /* Hq, multiple of num_kv_heads */
+  int32_t num_kv_heads; /* Hkv, 1 .. ALSPEC_MAX_KV_HEADS */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t kv_capacity;  /* L_cap: token stride of k and v */
+  const int32_t *seq_lens; /* host [B], 1 <= L_b <= L_cap */
+  int32_t kv_dtype;     /* alspec_kv_dtype */
+  int32_t sink;         /* S >= 0 */
+  int32_t window;       /* W >= 0, S + W >= 1 */
+  float sm_scale;       /* logit scale, > 0 and finite (normally 1/sqrt(D)) */
+  float lambda;         /* verify threshold, >= 0 (+inf allowed, NaN not) */
+  int32_t split_tokens;        /* middle split length; 0 = automatic */
+  int32_t window_split_tokens; /* window split length; 0 = automatic */
+} alspec_params;
+
+#define ALSPEC_MAX_BATCH 64
+#define ALSPEC_MAX_KV_HEADS 64
+/* group sizes G = Hq / Hkv that are built: 1, 2, 4, 8 */
+
+/* Optional timing events recorded around the fused call's kernels (any
+ * member may be NULL).  approx_* are recorded on the approximation stream,
+ * the others on the exact stream; exact_begin/exact_end bracket only the
+ * middle split-K kernel. */
+typedef struct {
+  void *approx_begin, *approx_end;
+  void *exact_begin, *exact_end;
+  void *verify_end;
+} alspec_events;
+
+typedef struct alspec_handle alspec_handle;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *alspec_status_string(alspec_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t alspec_version(void);
+
+/* Bytes of workspace the compute calls need for these parameters.  Pure
+ * host computation (no GPU needed); validates the parameters. */
+alspec_status alspec_workspace_size(const alspec_params *p, size_t *bytes);
+
+/* Inspection of the split plan (pure host): the splits of batch entry b in
+ * slot order, as kind (0 sink, 1 window, 2 middle) and token range
+ * [begin, end).  At most `cap` entries are written to the host arrays;
+ * *count receives the number of splits.  Also reports the chosen middle
+ * and window split lengths if the pointers are non-NULL. */
+alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
+                                 int32_t *kind, int32_t *begin, int32_t *end,
+                                 int32_t cap, int32_t *count,
+                                 int32_t *split_tokens,
+                                 int32_t *window_split_tokens);
+
+/* Create a handle bound to HIP device `device` (reads its properties and
+ * creates two events for cross-stream ordering).  *out is set on success. */
+alspec_status alspec_create(int device, alspec_handle **out);
+alspec_status alspec_destroy(alspec_handle *h);
+
+/*
+ * Attention-sink approximation ("a cheap attention-sink approximation",
+ * atlas.scime.ai summary, Approach): softmax attention of each query over
+ * the sink and window tokens only, renormalised over that set.  Writes
+ * o_approx [B][Hq][D] and, if non-NULL, lse_approx [B][Hq].  Also leaves in
+ * `ws` the per-split states of the sink and window tokens and their merged
+ * state, which alspec_lse_combine and the fused call reuse.
+ */
+alspec_status alspec_sink_approx(alspec_handle *h, const alspec_params *p,
+                                 const float *q, const void *k, const void *v,
+                                 float *o_approx, float *lse_approx, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/*
+ * Split-K flash decoding over the KV cache (flash decoding, which the pages
+ * list as a building block, atlas.scime.ai summary, "Builds on"): each
+ * (batch entry, kv head, token split) produces the softmax state
+ * (running max, normaliser, weighted value sum) of its G query heads, stored
+ * in `ws`.  include_sink_window = 1 computes every split (sink, window and
+ * middle); 0 computes the middle splits only, for use after
+ * alspec_sink_approx on the same workspace.
+ */
+alspec_status alspec_flash_decode_exact(alspec_handle *h,
+                                        const alspec_params *p,
+                                        const float *q, const void *k,
+                                        const void *v,
+                                        int32_t include_sink_window, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+/*
+ * Log-sum-exp combine of every split state of the plan held in `ws`
+ * (sink, window and middle splits, all of which must have been written)
+ * into exact attention: o_exact [B][Hq][D] and, if non-NULL,
+ * lse_exact [B][Hq].
+ */
+alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
+                                 const void *ws, size_t ws_bytes,
+                                 float *o_exact, float *lse_exact,
+                                 void *stream);
+
+/*
+ * Relative L2 verification ("verify with a relative L2 threshold to commit
+ * or discard", atlas.scime.ai summary, Approach): per batch entry b over
+ * its Hq*D outputs, ratio = ||o_approx - o_exact||_2 / ||o_exact||_2
+ * (0 if both norms are 0, +inf if only the exact norm is 0, NaN if any
+ * input is NaN) and commit = (ratio <= lambda).  If o_committed is non-NULL
+ * it receives o_approx for committed entries and o_exact otherwise.
+ */
+alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
+                            const float *o_approx, const float *o_exact,
+                            float *ratio, uint8_t *commit, float *o_committed,
+                            void *stream);
+
+/*
+ * The whole speculative step (atlas.scime.ai summary, Approach; ICML poster
+ * abstract: the approximation lets later work start early while exact
+ * attention runs, then a verify commits or discards).  On stream_approx:
+ * the sink and window splits and their merge, producing o_approx (and
+ * lse_approx if non-NULL); work enqueued on stream_approx after this call
+ * may consume o_approx.  On stream_exact: the middle splits, then (after
+ * the approximation's work) the merge with the reused sink/window state
+ * into o_exact (and lse_exact if non-NULL), the relative L2 verify into
+ * ratio and commit, and, if non-NULL, o_committed.  The call first orders
+ * stream_approx after the work already enqueued on stream_exact, so
+ * successive calls on the same workspace are safe.  The two streams may be
+ * the same stream.  `ev` may be NULL.
+ */
+alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
+                                 const float *q, const void *k, const void *v,
+                                 float *o_approx, float *lse_approx,
+                                 float *o_exact, float *lse_exact,
+                                 float *ratio, uint8_t *commit,
+                                 float *o_committed, void *ws,
+                                 size_t ws_bytes, void *stream_approx,
+                                 void *stream_exact, const alspec_events *ev);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ALSPEC_H */

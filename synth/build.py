@@ -1,0 +1,23 @@
+"""Build the device half of the input generator (libalspec_synth.so)."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "synth_kernels.hip")
+LIB = os.path.join(HERE, "libalspec_synth.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-o", LIB + ".tmp", SRC]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

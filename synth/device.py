@@ -1,0 +1,80 @@
+"""Draw a workload layer straight into device memory.
+
+ctypes front end of libalspec_synth.so, the device twin of gen.kv_slice.
+The host computes each head's planted rows and direction with gen.head_plant
+(so both sides share them exactly) and the kernel draws the bulk normals.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+from . import gen
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded)
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                f"{_build.LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(_build.LIB)
+        lib.synth_kv_fill.restype = ctypes.c_int
+        lib.synth_kv_fill.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+            ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def fill_kv(w: gen.Workload, layer: int, k, v, stream=None):
+    """Fill torch device tensors k, v ([B][Hkv][L_cap][D], float32 for an
+    f32 workload, bfloat16 for bf16) with the layer's keys and values."""
+    import torch
+    lib = _load()
+    bf16 = 1 if w.kv_dtype == "bf16" else 0
+    want = torch.bfloat16 if bf16 else torch.float32
+    for t in (k, v):
+        if (t.dtype != want or not t.is_contiguous() or
+                tuple(t.shape) != (w.B, w.Hkv, w.L_cap, w.D)):
+            raise ValueError("k/v tensor does not match the workload")
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    key = gen.layer_key(w.seed, layer)
+    sqrt_d = math.sqrt(w.D)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            p = gen.head_plant(w, layer, b, g)
+            u = np.ascontiguousarray(p.u, dtype=np.float64)
+            for tid, dst in ((gen.TENSOR_K, k), (gen.TENSOR_V, v)):
+                if tid == gen.TENSOR_K:
+                    rows = np.ascontiguousarray(p.bias_rows, dtype=np.int32)
+                    coef = np.ascontiguousarray(p.bias_coef, dtype=np.float64)
+                else:
+                    rows = np.zeros(0, np.int32)
+                    coef = np.zeros(0, np.float64)
+                rc = lib.synth_kv_fill(
+                    dst[b, g].data_ptr(), bf16, w.L_cap, w.D, key[0], key[1],
+                    g, tid, b, sqrt_d, int(rows.size), rows.ctypes.data,
+                    coef.ctypes.data, u.ctypes.data, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"synth_kv_fill failed: {rc}")
+
+
+def layer_to_device(w: gen.Workload, layer: int, device="cuda"):
+    """(q, k, v) torch tensors on the device for one layer."""
+    import torch
+    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    k = torch.empty((w.B, w.Hkv, w.L_cap, w.D), dtype=dt, device=device)
+    v = torch.empty_like(k)
+    fill_kv(w, layer, k, v)
+    q = torch.from_numpy(gen.q_all(w, layer)).to(device)
+    return q, k, v

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (no GPU needed): every function that
+include/alspec.h declares is exported by libalspec.so, parameters are
+validated before any GPU work, and the split plan tiles every context
+exactly into sink, window and middle ranges."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_level_speculation_amd as al
+from attention_level_speculation_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "alspec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(alspec_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("alspec_sink_approx", "alspec_flash_decode_exact",
+              "alspec_lse_combine", "alspec_verify", "alspec_spec_decode",
+              "alspec_workspace_size", "alspec_create", "alspec_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(al.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    for code, name in _binding.STATUS.items():
+        assert al.status_string(code) == name
+    assert al.status_string(99) == "ALSPEC_UNKNOWN_STATUS"
+    assert al.version() == 100
+
+
+def P(**kw):
+    args = dict(batch=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                kv_capacity=1000, seq_lens=[1000], kv_dtype="bf16", sink=4,
+                window=64, lam=0.1)
+    args.update(kw)
+    if "seq_lens" not in kw:
+        args["seq_lens"] = [args["kv_capacity"]] * args["batch"]
+    return al.make_params(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(num_q_heads=6, num_kv_heads=4), 1),
+    (dict(seq_lens=[0]), 1), (dict(seq_lens=[1001]), 1),
+    (dict(sink=0, window=0), 1), (dict(sink=-1), 1), (dict(window=-5), 1),
+    (dict(lam=-0.5), 1), (dict(lam=float("nan")), 1),
+    (dict(sm_scale=0.0), 1), (dict(sm_scale=float("inf")), 1),
+    (dict(kv_dtype=7), 1), (dict(split_tokens=-1), 1),
+    (dict(head_dim=96), 2), (dict(num_q_heads=48, num_kv_heads=2), 2),
+    (dict(batch=65, kv_capacity=10), 2), (dict(num_kv_heads=128,
+                                              num_q_heads=128), 2),
+])
+def test_workspace_size_validates(kw, status):
+    with pytest.raises(al.AlspecError) as e:
+        al.workspace_size(P(**kw))
+    assert e.value.status == status
+
+
+def test_lambda_inf_is_accepted():
+    assert al.workspace_size(P(lam=float("inf"))) > 0
+
+
+def test_null_handle_and_pointers_rejected_before_gpu_work():
+    p = P()
+    f = _binding._spec_decode
+    st = f(None, ctypes.byref(p), *([None] * 11), 0, None, None, None)
+    assert st == 1
+    assert _binding._sink_approx(None, ctypes.byref(p), None, None, None,
+                                 None, None, None, 0, None) == 1
+    assert _binding._verify(None, ctypes.byref(p), None, None, None, None,
+                            None, None) == 1
+    assert _binding._lse_combine(None, ctypes.byref(p), None, 0, None, None,
+                                 None) == 1
+    assert _binding._flash_exact(None, ctypes.byref(p), None, None, None, 0,
+                                 None, 0, None) == 1
+    n = ctypes.c_size_t()
+    assert _binding._workspace_size(None, ctypes.byref(n)) == 1
+
+
+def _check_tiling(p, b, L, S, W):
+    splits, (T, Tw) = al.plan_splits(p, b)
+    s_end = min(S, L)
+    w_begin = max(s_end, L - W)
+    kinds = [k for k, _, _ in splits]
+    assert kinds == sorted(kinds), "slot order must be sink, window, middle"
+    # every token of [0, L) exactly once
+    cover = np.zeros(L, np.int32)
+    for kd, t0, t1 in splits:
+        assert 0 <= t0 < t1 <= L
+        cover[t0:t1] += 1
+        if kd == 0:
+            assert (t0, t1) == (0, s_end)
+        elif kd == 1:
+            assert w_begin <= t0 and t1 <= L and t1 - t0 <= Tw
+        else:
+            assert s_end <= t0 and t1 <= w_begin and t1 - t0 <= T
+    assert (cover == 1).all()
+    assert sum(1 for k in kinds if k == 0) == (1 if s_end > 0 else 0)
+    win = sorted((t0, t1) for kd, t0, t1 in splits if kd == 1)
+    mid = sorted((t0, t1) for kd, t0, t1 in splits if kd == 2)
+    if win:
+        assert win[0][0] == w_begin and win[-1][1] == L
+    if mid:
+        assert mid[0][0] == s_end and mid[-1][1] == w_begin
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_split_plan_tiles_context(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 9))
+    L_cap = int(rng.choice([1, 7, 64, 1000, 4097, 131072]))
+    lens = [int(x) for x in rng.integers(1, L_cap + 1, size=B)]
+    S = int(rng.integers(0, 9))
+    W = int(rng.choice([0, 1, 63, 128, 2048, 5000]))
+    if S + W == 0:
+        W = 1
+    split = int(rng.choice([0, 0, 64, 300, 1024]))
+    wsplit = int(rng.choice([0, 0, 32, 100]))
+    p = al.make_params(B, 8, 4, 64, L_cap, lens, "f32", S, W, 0.1,
+                       split_tokens=split, window_split_tokens=wsplit)
+    for b in range(B):
+        _check_tiling(p, b, lens[b], S, W)
+    assert al.workspace_size(p) > 0
+
+
+def test_headline_plan_shape():
+    """Context 131072, S 4, W 2048, 8 kv heads: one sink split, window cut
+    into 16 pieces of 128, middle pieces of the automatic length."""
+    p = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1)
+    splits, (T, Tw) = al.plan_splits(p, 0)
+    assert Tw == 128 and T in (256, 512, 1024, 2048)
+    assert sum(1 for s in splits if s[0] == 1) == 16
+    _check_tiling(p, 0, 131072, 4, 2048)
+
+
+def test_workspace_grows_with_splits():
+    a = al.workspace_size(P(split_tokens=1024))
+    b = al.workspace_size(P(split_tokens=64))
+    assert b > a

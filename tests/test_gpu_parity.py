@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars: per (user, layer) relative L2 error of O_exact and O_approx <= 1e-5
+with fp32 KV and <= 2e-3 with bf16 KV (fp32 accumulation); |ratio - ratio
+oracle| <= 1e-4; commit flags equal except where the oracle's ratio lies
+within 1e-4 of lambda; lse within 1e-4 nats; the committed output is
+exactly the approximate or the exact output.  Full-size cases use the
+automatic split plan, the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import attention_level_speculation_amd as al  # noqa: E402
+import oracle  # noqa: E402
+from synth import gen  # noqa: E402
+
+from gpu_util import (compare, run_fused, run_standalone,  # noqa: E402
+                      to_device)
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h = al.Handle(0)
+    yield h
+    h.close()
+
+
+def _case(handle, w, layer=0, lam=None, two_streams=True, **pkw):
+    lam = w.lam if lam is None else lam
+    print(f"[case] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+          f"lens={w.seq_lens[:4]}{'...' if w.B > 4 else ''} {w.kv_dtype} "
+          f"S={w.S} W={w.W} lam={lam} layer={layer} {pkw}", flush=True)
+    q, k, v = gen.layer_inputs(w, layer)
+    ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, lam)
+    p = al.params_for(w, lam=lam, **pkw)
+    qd, kd, vd = to_device(q, k, v)
+    got = run_fused(al, handle, p, qd, kd, vd, two_streams=two_streams)
+    worst = compare(got, ref, w.kv_dtype, lam, w.name)
+    print(f"[case] worst {worst} ratio gpu {got['ratio'][:4]} oracle "
+          f"{ref['ratio'][:4]}", flush=True)
+    return q, k, v, ref, got, p, (qd, kd, vd)
+
+
+# ------------------------------------------------------ workload configs ---
+
+def test_tiny_f32(handle):
+    _case(handle, gen.tiny_f32_1k())
+
+
+def test_tiny_f32_standalone_path(handle):
+    w = gen.tiny_f32_1k()
+    q, k, v = gen.layer_inputs(w, 0)
+    ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam)
+    p = al.params_for(w)
+    qd, kd, vd = to_device(q, k, v)
+    got = run_standalone(al, handle, p, qd, kd, vd)
+    compare(got, ref, "f32", w.lam, "standalone")
+    got2 = run_standalone(al, handle, p, qd, kd, vd, include_sink_window=True)
+    compare(got2, ref, "f32", w.lam, "standalone-all-splits")
+    # the exact splits recomputed over sink+window give the same bits
+    assert np.array_equal(got["o_exact"], got2["o_exact"])
+    fused = run_fused(al, handle, p, qd, kd, vd)
+    assert np.array_equal(fused["o_approx"], got["o_approx"])
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_llama8b_32k_layers(handle, layer):
+    _case(handle, gen.llama8b_32k(), layer=layer)
+
+
+def test_headline_128k_full_size(handle):
+    _case(handle, gen.llama8b_128k(needles=4), layer=0)
+
+
+@pytest.mark.parametrize("needles", [0, 16])
+def test_headline_density_extremes_scaled(handle, needles):
+    w = gen.scaled(gen.llama8b_128k(needles=needles), 20000)
+    for layer in range(3):
+        _case(handle, w, layer=layer)
+
+
+def test_multiuser_ragged_full_size(handle):
+    w = gen.multiuser_8b()
+    q, k, v = gen.layer_inputs(w, 0)
+    qd, kd, vd = to_device(q, k, v)
+    for lam in (0.05, 0.10, 0.20):
+        print(f"[case] multiuser lam={lam} lens={w.seq_lens}", flush=True)
+        ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, lam)
+        p = al.params_for(w, lam=lam)
+        got = run_fused(al, handle, p, qd, kd, vd)
+        compare(got, ref, "bf16", lam, f"multiuser lam={lam}")
+        print(f"[case] commits {got['commit'].tolist()} oracle "
+              f"{ref['commit'].tolist()}", flush=True)
+
+
+def test_llama70b_full_size(handle):
+    _case(handle, gen.llama70b_128k(), layer=0)
+
+
+# ------------------------------------------------------------ edge cases ---
+
+def _mk(name, B, Hq, Hkv, D, lens, dt, S, W, lam=0.1, needles=1, seed=7):
+    return gen.Workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, L_cap=max(lens),
+                        seq_lens=list(lens), kv_dtype=dt, S=S, W=W, lam=lam,
+                        needles=[needles] * B, seed=seed)
+
+
+EDGE = [
+    # name, B, Hq, Hkv, D, lens, dtype, S, W, split, wsplit
+    ("g1_d64_f32", 2, 4, 4, 64, [777, 1500], "f32", 4, 100, 0, 0),
+    ("g2_d128_bf16", 2, 8, 4, 128, [3001, 65], "bf16", 4, 256, 0, 0),
+    ("g4_d64_bf16", 3, 8, 2, 64, [2049, 1, 300], "bf16", 4, 128, 0, 0),
+    ("g8_d128_f32", 1, 16, 2, 128, [5003], "f32", 4, 512, 256, 64),
+    ("g8_d64_bf16", 2, 8, 1, 64, [4100, 999], "bf16", 2, 200, 0, 0),
+    ("tiny_splits", 2, 8, 2, 128, [1234, 4321], "bf16", 4, 300, 64, 32),
+    ("odd_splits", 1, 4, 2, 128, [6000], "f32", 3, 333, 777, 50),
+    ("no_sink", 2, 8, 2, 128, [2000, 1500], "bf16", 0, 300, 0, 0),
+    ("no_window", 2, 8, 2, 128, [2000, 1500], "bf16", 4, 0, 0, 0),
+    ("short_inside_sink", 3, 8, 2, 64, [1, 2, 3], "f32", 4, 0, 0, 0),
+    ("cover_exact", 2, 8, 2, 128, [132, 100], "bf16", 4, 128, 0, 0),
+    ("window_only_long", 1, 8, 8, 128, [4096], "bf16", 0, 1, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(handle, case):
+    name, B, Hq, Hkv, D, lens, dt, S, W, split, wsplit = case
+    w = _mk(name, B, Hq, Hkv, D, lens, dt, S, W)
+    q, k, v, ref, got, p, dev = _case(handle, w, split_tokens=split,
+                                      window_split_tokens=wsplit)
+    stand = run_standalone(al, handle, p, *dev)
+    compare(stand, ref, dt, w.lam, name + "-standalone")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_full_cover_gives_ratio_exactly_zero(handle, dt):
+    """S + W >= L: the middle is empty, the exact merge repeats the
+    approximation's operations, so the outputs agree bit for bit and the
+    ratio is exactly 0 (commit even at lambda = 0)."""
+    w = _mk("cover", 3, 8, 2, 128, [200, 64, 131], dt, 4, 196, lam=0.0)
+    q, k, v = gen.layer_inputs(w, 0)
+    p = al.params_for(w, lam=0.0)
+    dev = to_device(q, k, v)
+    for two in (True, False):
+        got = run_fused(al, handle, p, *dev, two_streams=two)
+        assert np.array_equal(got["o_exact"], got["o_approx"])
+        assert (got["ratio"] == 0).all() and (got["commit"] == 1).all()
+    st = run_standalone(al, handle, p, *dev)
+    assert np.array_equal(st["o_exact"], st["o_approx"])
+    assert (st["ratio"] == 0).all() and (st["commit"] == 1).all()
+
+
+def test_nan_user_discards_others_unchanged(handle):
+    w = _mk("nan", 3, 8, 2, 128, [3000, 3000, 3000], "bf16", 4, 256)
+    q, k, v = gen.layer_inputs(w, 0)
+    p = al.params_for(w, lam=math.inf)
+    base = run_fused(al, handle, p, *to_device(q, k, v))
+    k2 = k.copy()
+    v2 = v.copy()
+    nan_bf16 = np.uint16(0x7FC0)
+    k2[1, 0, 1500, 3] = nan_bf16       # middle key of entry 1
+    v2[2, 1, 1, 0] = nan_bf16          # sink value of entry 2
+    got = run_fused(al, handle, p, *to_device(q, k2, v2))
+    assert got["commit"].tolist() == [1, 0, 0]
+    assert math.isnan(got["ratio"][1]) and math.isnan(got["ratio"][2])
+    for key in ("o_exact", "o_approx", "ratio", "o_committed"):
+        assert np.array_equal(got[key][0], base[key][0])
+
+
+def test_padding_rows_never_read(handle):
+    """Rows at or beyond an entry's length hold NaN; nothing changes."""
+    w = _mk("pad", 3, 8, 2, 128, [1000, 2500, 4096], "bf16", 4, 300)
+    q, k, v = gen.layer_inputs(w, 0)
+    k2 = k.copy()
+    v2 = v.copy()
+    for b, L in enumerate(w.seq_lens):
+        k2[b, :, L:] = np.uint16(0x7FC0)
+        v2[b, :, L:] = np.uint16(0x7FC0)
+    p = al.params_for(w)
+    a = run_fused(al, handle, p, *to_device(q, k, v))
+    b_ = run_fused(al, handle, p, *to_device(q, k2, v2))
+    for key in ("o_exact", "o_approx", "ratio", "commit"):
+        assert np.array_equal(a[key], b_[key]), key
+
+
+def test_lambda_extremes(handle):
+    w = _mk("lam", 4, 8, 2, 64, [900, 1200, 50, 3000], "f32", 4, 60)
+    q, k, v = gen.layer_inputs(w, 0)
+    dev = to_device(q, k, v)
+    g_inf = run_fused(al, handle, al.params_for(w, lam=math.inf), *dev)
+    assert (g_inf["commit"] == 1).all()
+    g_0 = run_fused(al, handle, al.params_for(w, lam=0.0), *dev)
+    assert g_0["commit"].tolist() == [int(r == 0) for r in g_0["ratio"]]
+    assert g_0["commit"][2] == 1  # L = 50 <= S + W: exact cover
+
+
+def test_determinism_and_one_vs_two_streams(handle):
+    w = gen.scaled(gen.llama8b_32k(), 9000, seq_lens=[9000])
+    q, k, v = gen.layer_inputs(w, 0)
+    p = al.params_for(w)
+    dev = to_device(q, k, v)
+    a = run_fused(al, handle, p, *dev, two_streams=True)
+    b = run_fused(al, handle, p, *dev, two_streams=True)
+    c = run_fused(al, handle, p, *dev, two_streams=False)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(a[key], c[key]), key
+
+
+def test_back_to_back_calls_share_workspace(handle):
+    """Successive fused calls on one workspace and two streams, with
+    different inputs, each match their own single-call result."""
+    w = gen.scaled(gen.llama8b_32k(), 6000)
+    p = al.params_for(w)
+    ws = al.alloc_workspace(p)
+    sa, se = torch.cuda.Stream(), torch.cuda.Stream()
+    layers = [to_device(*gen.layer_inputs(w, l)) for l in range(3)]
+    outs = []
+    for dev in layers:
+        o = al.alloc_outputs(p)
+        al.spec_decode(handle, p, *dev, o, ws, sa, se)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for dev, o in zip(layers, outs):
+        ref = run_fused(al, handle, p, *dev)
+        for key in ref:
+            assert np.array_equal(o[key].cpu().numpy(), ref[key]), key
+
+
+def test_workspace_reuse_across_shapes(handle):
+    big = gen.scaled(gen.llama8b_32k(), 8000)
+    small = _mk("small", 2, 16, 2, 64, [700, 1300], "f32", 4, 64)
+    pb = al.params_for(big)
+    ps = al.params_for(small)
+    ws = al.alloc_workspace(pb)
+    assert ws.numel() >= al.workspace_size(ps)
+    for w, p in ((big, pb), (small, ps), (big, pb)):
+        q, k, v = gen.layer_inputs(w, 0)
+        ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam)
+        got = run_fused(al, handle, p, *to_device(q, k, v), ws=ws)
+        compare(got, ref, w.kv_dtype, w.lam, "reuse " + w.name)
+
+
+def test_invalid_workspace_rejected(handle):
+    w = _mk("ws", 1, 8, 2, 128, [500], "bf16", 4, 64)
+    q, k, v = gen.layer_inputs(w, 0)
+    p = al.params_for(w)
+    dev = to_device(q, k, v)
+    ws = al.alloc_workspace(p)
+    out = al.alloc_outputs(p)
+    with pytest.raises(al.AlspecError) as e:
+        al.spec_decode(handle, p, *dev, out, ws[:-256])
+    assert e.value.status == 3
+    with pytest.raises(al.AlspecError) as e:
+        al.spec_decode(handle, p, *dev, out, ws[1:])
+    assert e.value.status == 3
