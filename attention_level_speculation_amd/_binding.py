@@ -42,7 +42,8 @@ class Params(ctypes.Structure):
                 ("kv_capacity", _i32), ("seq_lens", ctypes.POINTER(_i32)),
                 ("kv_dtype", _i32), ("sink", _i32), ("window", _i32),
                 ("sm_scale", ctypes.c_float), ("lam", ctypes.c_float),
-                ("split_tokens", _i32), ("window_split_tokens", _i32)]
+                ("split_tokens", _i32), ("window_split_tokens", _i32),
+                ("overlap", _i32)]
 
 
 class Events(ctypes.Structure):
@@ -104,7 +105,7 @@ def _check(st, what):
 
 def make_params(batch, num_q_heads, num_kv_heads, head_dim, kv_capacity,
                 seq_lens, kv_dtype, sink, window, lam, sm_scale=None,
-                split_tokens=0, window_split_tokens=0):
+                split_tokens=0, window_split_tokens=0, overlap=0):
     """Build an alspec_params.  kv_dtype is "f32" or "bf16" (or 0/1).  The
     returned struct keeps its host seq_lens array alive."""
     if isinstance(kv_dtype, str):
@@ -116,7 +117,7 @@ def make_params(batch, num_q_heads, num_kv_heads, head_dim, kv_capacity,
                int(head_dim), int(kv_capacity),
                ctypes.cast(lens, ctypes.POINTER(_i32)), int(kv_dtype),
                int(sink), int(window), float(sm_scale), float(lam),
-               int(split_tokens), int(window_split_tokens))
+               int(split_tokens), int(window_split_tokens), int(overlap))
     p._lens = lens  # keep alive
     return p
 
@@ -310,7 +311,8 @@ def spec_decode(h, p, q, k, v, out, ws, stream_approx=None,
                 stream_exact=None, events=None):
     """Fused step.  `out` is a dict as made by alloc_outputs (lse_* and
     o_committed may be None).  `events`: dict of torch.cuda.Event by
-    alspec_events member name, or None."""
+    alspec_events member name, or None; each event must have been recorded
+    once already (torch creates the underlying hipEvent on first record)."""
     torch = _torch()
     qp, kp, vp = _qkv(p, q, k, v)
     B, Hq, D = p.batch, p.num_q_heads, p.head_dim

@@ -34,6 +34,13 @@ alspec_status check_inputs(const float *q, const void *k, const void *v) {
   return ALSPEC_OK;
 }
 
+// Output arrays are written with 16-byte vector stores.
+alspec_status check_outputs(const float *a, const float *b, const float *c) {
+  if ((a && !aligned(a, 16)) || (b && !aligned(b, 16)) || (c && !aligned(c, 16)))
+    return ALSPEC_ERR_INVALID_ARG;
+  return ALSPEC_OK;
+}
+
 alspec_status check_ws(const void *ws, size_t ws_bytes,
                        const alspec::Workspace &wl) {
   if (!ws) return ALSPEC_ERR_WORKSPACE;
@@ -160,9 +167,12 @@ alspec_status alspec_sink_approx(alspec_handle *h, const alspec_params *p,
   if ((st = check_inputs(q, k, v)) != ALSPEC_OK) return st;
   if ((st = check_ws(ws, ws_bytes, wl)) != ALSPEC_OK) return st;
   const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
+  alspec::Outs o{};
+  o.o_approx = o_approx;
+  o.lse_approx = lse_approx;
   return hip_status(alspec::launch_partials(
-      pa, p->kv_dtype, true, true, q, k, v, p->sm_scale * kLog2e, w, o_approx,
-      lse_approx, (hipStream_t)stream));
+      pa, p->kv_dtype, alspec::kPartialsApprox, true, q, k, v,
+      p->sm_scale * kLog2e, w, o, (hipStream_t)stream));
 }
 
 alspec_status alspec_flash_decode_exact(alspec_handle *h,
@@ -183,14 +193,16 @@ alspec_status alspec_flash_decode_exact(alspec_handle *h,
   const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
   const float sm_log2 = p->sm_scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
+  const alspec::Outs none{};
   if (include_sink_window) {
-    hipError_t e = alspec::launch_partials(pa, p->kv_dtype, true, false, q, k,
-                                           v, sm_log2, w, nullptr, nullptr, s);
+    hipError_t e =
+        alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates,
+                                true, q, k, v, sm_log2, w, none, s);
     if (e != hipSuccess) return ALSPEC_ERR_HIP;
   }
-  return hip_status(alspec::launch_partials(pa, p->kv_dtype, false, false, q,
-                                            k, v, sm_log2, w, nullptr,
-                                            nullptr, s));
+  return hip_status(alspec::launch_partials(pa, p->kv_dtype,
+                                            alspec::kPartialsStates, false, q,
+                                            k, v, sm_log2, w, none, s));
 }
 
 alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
@@ -238,6 +250,8 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   alspec_status st = alspec::make_plan(p, &pa, &wl);
   if (st != ALSPEC_OK) return st;
   if ((st = check_inputs(q, k, v)) != ALSPEC_OK) return st;
+  if ((st = check_outputs(o_approx, o_exact, o_committed)) != ALSPEC_OK)
+    return st;
   if ((st = check_ws(ws, ws_bytes, wl)) != ALSPEC_OK) return st;
   const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
   const float sm_log2 = p->sm_scale * kLog2e;
@@ -247,32 +261,60 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   alspec_events none;
   memset(&none, 0, sizeof none);
   const alspec_events &E = ev ? *ev : none;
+  alspec::Outs o{o_approx, lse_approx, o_exact, lse_exact, ratio,
+                 commit,   o_committed, p->lambda};
 
-  // The approximation reuses this workspace: order it after everything the
-  // exact stream already holds (earlier calls' merges read the workspace).
+  if (!p->overlap) {
+    // Approximation first, then the exact pass, in one stream: no
+    // cross-stream wait between the kernels.  The approximation stream is
+    // handed o_approx through an event, so work queued there after this
+    // call runs while the exact pass does.
+    if ((st = record(E.approx_begin, se)) != ALSPEC_OK) return st;
+    if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsApprox,
+                                true, q, k, v, sm_log2, w, o,
+                                se) != hipSuccess)
+      return ALSPEC_ERR_HIP;
+    if ((st = record(E.approx_end, se)) != ALSPEC_OK) return st;
+    if (two) {
+      if (hipEventRecord(h->ev_approx, se) != hipSuccess) return ALSPEC_ERR_HIP;
+      if (hipStreamWaitEvent(sa, h->ev_approx, 0) != hipSuccess)
+        return ALSPEC_ERR_HIP;
+    }
+    if ((st = record(E.exact_begin, se)) != ALSPEC_OK) return st;
+    if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates,
+                                false, q, k, v, sm_log2, w, o,
+                                se) != hipSuccess)
+      return ALSPEC_ERR_HIP;
+    if ((st = record(E.exact_end, se)) != ALSPEC_OK) return st;
+    if (alspec::launch_merge_verify(pa, w, o, se) != hipSuccess)
+      return ALSPEC_ERR_HIP;
+    return record(E.verify_end, se);
+  }
+
+  // Overlap: the approximation (on stream_approx) and the middle splits (on
+  // stream_exact) start together; the exact merge waits for both.  The
+  // approximation reuses this workspace, so it is first ordered after
+  // everything the exact stream already holds (earlier calls' merges).
   if (two) {
     if (hipEventRecord(h->ev_join, se) != hipSuccess) return ALSPEC_ERR_HIP;
     if (hipStreamWaitEvent(sa, h->ev_join, 0) != hipSuccess)
       return ALSPEC_ERR_HIP;
   }
   if ((st = record(E.approx_begin, sa)) != ALSPEC_OK) return st;
-  if (alspec::launch_partials(pa, p->kv_dtype, true, true, q, k, v, sm_log2,
-                              w, o_approx, lse_approx, sa) != hipSuccess)
+  if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsApprox, true,
+                              q, k, v, sm_log2, w, o, sa) != hipSuccess)
     return ALSPEC_ERR_HIP;
   if ((st = record(E.approx_end, sa)) != ALSPEC_OK) return st;
   if (two && hipEventRecord(h->ev_approx, sa) != hipSuccess)
     return ALSPEC_ERR_HIP;
-
   if ((st = record(E.exact_begin, se)) != ALSPEC_OK) return st;
-  if (alspec::launch_partials(pa, p->kv_dtype, false, false, q, k, v, sm_log2,
-                              w, nullptr, nullptr, se) != hipSuccess)
+  if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates, false,
+                              q, k, v, sm_log2, w, o, se) != hipSuccess)
     return ALSPEC_ERR_HIP;
   if ((st = record(E.exact_end, se)) != ALSPEC_OK) return st;
   if (two && hipStreamWaitEvent(se, h->ev_approx, 0) != hipSuccess)
     return ALSPEC_ERR_HIP;
-  if (alspec::launch_merge_verify(pa, w, o_approx, o_exact, lse_exact, ratio,
-                                  commit, o_committed, p->lambda,
-                                  se) != hipSuccess)
+  if (alspec::launch_merge_verify(pa, w, o, se) != hipSuccess)
     return ALSPEC_ERR_HIP;
   return record(E.verify_end, se);
 }

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stdint.h>
+
 #include "alspec_plan.h"
 
 namespace alspec {
@@ -20,22 +22,31 @@ struct WsPtrs {
 
 WsPtrs ws_ptrs(void *ws, const Workspace &wl);
 
-// Split states over the sink and window splits (approx_set = true) or the
-// middle splits (false).  With `combine`, the last block of each
-// (entry, kv head) merges its sink+window states into o_approx, lse_approx
-// (may be null) and the merged state in the workspace.
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
-                           bool combine, const float *q, const void *k,
+// Output buffers of the merging kernel modes (any may be null where a
+// mode does not write it; lse_* and o_committed are always optional).
+struct Outs {
+  float *o_approx, *lse_approx, *o_exact, *lse_exact, *ratio;
+  uint8_t *commit;
+  float *o_committed;
+  float lambda;
+};
+
+enum PartialsMode {
+  kPartialsStates = 0,  // split states only (sink+window or middle)
+  kPartialsApprox = 1   // sink+window states, merged into o_approx
+};
+
+// Split-state kernel over the sink and window splits (approx_set = true;
+// implied by kPartialsApprox) or the middle splits.
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, int mode,
+                           bool approx_set, const float *q, const void *k,
                            const void *v, float sm_log2, const WsPtrs &w,
-                           float *o_approx, float *lse_approx, hipStream_t s);
+                           const Outs &o, hipStream_t s);
 
 // Exact merge of the stored sink+window state with the middle splits, then
-// the relative L2 verify, the commit flag and the committed output.
+// the relative L2 verify, the commit flag and the committed output (o.*).
 hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
-                               const float *o_approx, float *o_exact,
-                               float *lse_exact, float *ratio, uint8_t *commit,
-                               float *o_committed, float lambda,
-                               hipStream_t s);
+                               const Outs &o, hipStream_t s);
 
 // Exact merge of every split state of the plan.
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,

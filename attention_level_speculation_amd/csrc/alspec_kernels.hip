@@ -17,6 +17,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "alspec_kernels.h"
 
 namespace alspec {
@@ -253,68 +255,371 @@ __device__ void split_state(const float *__restrict__ qg,
   }
 }
 
+// --------------------------------------- one split of one head, MFMA QK ---
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// float32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// x = hi + mid + lo with each part a bf16: every step takes the exact fp32
+// residual of the previous one, so the three parts carry x to within
+// 2^-24 |x|, the precision of x itself.
+__device__ __forceinline__ void split3(const float *x, bf16x8 &hi,
+                                       bf16x8 &mid, bf16x8 &lo) {
+  u32x4 h, m, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t hp[2], mp[2], lp[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = x[2 * i + e];
+      hp[e] = bf16_rne(v);
+      const float r1 = v - __uint_as_float(hp[e] << 16);
+      mp[e] = bf16_rne(r1);
+      const float r2 = r1 - __uint_as_float(mp[e] << 16);
+      lp[e] = bf16_rne(r2);
+    }
+    h[i] = hp[0] | (hp[1] << 16);
+    m[i] = mp[0] | (mp[1] << 16);
+    l[i] = lp[0] | (lp[1] << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  mid = __builtin_bit_cast(bf16x8, m);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Softmax state of the G (4 or 8) query heads of one kv head over tokens
+// [t0, t1), bf16 K/V with D = 128.  The logit block S^T = K_tile Q^T of a
+// 16-token tile is one 16x16 output of v_mfma_f32_16x16x32_bf16 per
+// 32-wide slice of D (K rows are the A operand straight from HBM, the
+// query heads the B operand, padded to 16 columns).  q is split into three
+// bf16 parts whose products accumulate in fp32, so the logits keep fp32
+// accuracy.  Lane l (r = l % 16, c = l / 16) loads bytes [64c, 64c + 64) of
+// tile row r, and both operands map slice s, element j to
+// d = 32c + 8s + j.  The output gives lane l the logits of tokens 4c + j
+// (j = 0..3) for head r.  P*V runs on the VALU: lane l owns d = 8r..8r+7
+// of V rows 4c + j and reads the G probabilities of its rows from LDS.
+// Wave w takes tiles w, w + 4, ... of the range; the next tile's K and V
+// are loaded while the current one is computed.  Each wave keeps its own
+// online softmax; the waves are merged at the end.
+template <int G>
+__device__ void split_state_mfma(const float *__restrict__ qg,
+                                 const uint16_t *__restrict__ kb,
+                                 const uint16_t *__restrict__ vb, int t0,
+                                 int t1, float sm_log2,
+                                 float2 *__restrict__ out_ml,
+                                 float *__restrict__ out_acc) {
+  static_assert(G == 4 || G == 8, "MFMA path serves groups of 4 or 8");
+  constexpr int D = 128;
+  constexpr int TILE = 16;
+  constexpr int STEP = kWaves * TILE;
+
+  __shared__ float s_p[kWaves][4][4][G];  // [wave][c][j][head]
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ float s_acc[kWaves][G][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int c = lane >> 4;
+
+  float m_lane = neg_inf();  // running max of head r (same in all 4 rows)
+  float l_lane = 0.f;        // this lane's share of head r's normaliser
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+
+  auto load = [&](int tb, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
+    const int krow = tb + r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kk[s] = u32x4{0u, 0u, 0u, 0u};
+      if (krow < t1)
+        kk[s] = *(const u32x4 *)(kb + (size_t)krow * D + 32 * c + 8 * s);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vrow = tb + 4 * c + j;
+      vv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (vrow < t1) vv[j] = *(const u32x4 *)(vb + (size_t)vrow * D + 8 * r);
+    }
+  };
+
+  // The first tile's loads go out before q is read and split, so the two
+  // round trips overlap.
+  u32x4 kr[4], vr[4];
+  load(t0 + wave * TILE, kr, vr);
+
+  // q of head r (columns r >= G are padding: a valid row is read and
+  // zeroed, so the loads need no branch and go out together)
+  bf16x8 qh[4], qm[4], ql[4];
+  {
+    const float4 *qr =
+        (const float4 *)(qg + (size_t)(r < G ? r : G - 1) * D + 32 * c);
+    const float qs = r < G ? sm_log2 : 0.f;
+    float4 qv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = qr[i];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float x[8] = {qv[2 * s].x * qs,     qv[2 * s].y * qs,
+                          qv[2 * s].z * qs,     qv[2 * s].w * qs,
+                          qv[2 * s + 1].x * qs, qv[2 * s + 1].y * qs,
+                          qv[2 * s + 1].z * qs, qv[2 * s + 1].w * qs};
+      split3(x, qh[s], qm[s], ql[s]);
+    }
+  }
+
+  for (int blk = t0; blk < t1; blk += STEP) {
+    const int tb = blk + wave * TILE;
+    // next tile (rows at or past t1 are not read and come back as zero)
+    u32x4 kn[4], vn[4];
+    load(tb + STEP, kn, vn);
+    // logits: lane holds tokens 4c + j of the tile for head r
+    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[s]);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qh[s], a4, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qm[s], a4, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, ql[s], a4, 0, 0, 0);
+    }
+    float sv[4];
+    float mx = neg_inf();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sv[j] = (tb + 4 * c + j < t1) ? a4[j] : neg_inf();
+      mx = fmaxf(mx, sv[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m_lane, mx);
+    const float ref = exp_ref(mnew);
+    const float sc = fast_exp2(m_lane - ref);
+    m_lane = mnew;
+    float ls = l_lane * sc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pj = fast_exp2(sv[j] - ref);
+      ls += pj;
+      if (r < G) s_p[wave][c][j][r] = pj;
+    }
+    l_lane = ls;
+    // rescale: head h's factor is uniform, held by lane h
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sh = readlane_f(sc, h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] *= sh;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float vf[8];
+      KvBf16::unpack(__builtin_bit_cast(uint4, vr[j]), vf);
+      float pv[G];
+#pragma unroll
+      for (int h4 = 0; h4 < G; h4 += 4) {
+        const float4 p4 = *(const float4 *)&s_p[wave][c][j][h4];
+        pv[h4] = p4.x;
+        pv[h4 + 1] = p4.y;
+        pv[h4 + 2] = p4.z;
+        pv[h4 + 3] = p4.w;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kr[s] = kn[s];
+      vr[s] = vn[s];
+    }
+  }
+
+  // Sum the four row groups (same running max in every row).
+  l_lane += __shfl_xor(l_lane, 16);
+  l_lane += __shfl_xor(l_lane, 32);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[h][i] += __shfl_xor(acc[h][i], 16);
+      acc[h][i] += __shfl_xor(acc[h][i], 32);
+    }
+  if (c == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_acc[wave][h][8 * r + i] = acc[h][i];
+    if (r < G) {
+      s_m[wave][r] = m_lane;
+      s_l[wave][r] = l_lane;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    const float ref = exp_ref(M);
+    float ls = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sw = fast_exp2(s_m[w][h] - ref);
+      ls += s_l[w][h] * sw;
+      a += s_acc[w][h][d] * sw;
+    }
+    out_acc[h * D + d] = a;
+    if (d == 0) out_ml[h] = make_float2(M, ls);
+  }
+}
+
 // ------------------------------------------------------- merge of splits ---
 
-// Merge the states of query head h of one batch entry: an optional prior
-// state, then slots [slot0, slot0 + n) (stride Hq in ml, Hq * D in acc).
-// All threads of the block take part.  On return res_acc[0..D) (shared),
-// *res_m and *res_l (shared) hold the merged state.  The sum order is a
-// fixed function of n, so equal inputs give equal bits.
-template <int D>
-__device__ void merge_head(const float2 *__restrict__ ml,
-                           const float *__restrict__ acc, int slot0, int n,
-                           int Hq, int h, bool has_prior, float2 prior_ml,
-                           const float *__restrict__ prior_acc,
-                           float *res_acc, float *res_m, float *res_l) {
-  constexpr int CH = D / 4;            // float4 chunks of a row
-  constexpr int NSG = kThreads / CH;   // slot groups
-  __shared__ float s_red[kWaves];
-  __shared__ float s_pl[NSG];
-  __shared__ float4 s_pacc[NSG][CH];
+// Merge the states of NH consecutive query heads h0.. of one batch entry:
+// an optional prior state per head, then slots [slot0, slot0 + n) (stride
+// Hq in ml, Hq * D in acc).  The block's threads split into NH heads x NSG
+// slot groups x D/4 float4 chunks; slot i goes to group i % NSG, each group
+// sums its slots in increasing order, and the groups are then added in
+// order after the prior, so the bits depend only on (n, NH, D).  prior_ml
+// and prior_acc must be valid addresses even when has_prior is false.  Up to
+// NSG * R slots are merged in one memory round: every thread issues all
+// its loads (which also cover every slot's max) before using any.  Larger
+// n takes a max pass and then rounds of NSG * R slots.  On return
+// res_acc[NH][D], res_m[NH], res_l[NH] (shared) hold the merged states.
+template <int D, int NH, int R>
+__device__ void merge_heads(const float2 *__restrict__ ml,
+                            const float *__restrict__ acc, int slot0, int n,
+                            int Hq, int h0, bool has_prior,
+                            const float2 *__restrict__ prior_ml,
+                            const float *__restrict__ prior_acc,
+                            float *res_acc, float *res_m, float *res_l) {
+  constexpr int CH = D / 4;
+  constexpr int TPH = kThreads / NH;  // threads per head
+  constexpr int NSG = TPH / CH;       // slot groups per head
+  static_assert(NSG >= 1 && NSG * CH * NH == kThreads, "thread split");
+  constexpr int WPH = TPH >= 64 ? TPH / 64 : 1;  // waves per head
+  __shared__ float s_mx[NH][WPH];
+  __shared__ float4 s_pacc[NH][NSG][CH];
+  __shared__ float s_pl[NH][NSG];
 
   const int t = threadIdx.x;
-  // global max
-  float mx = has_prior ? prior_ml.x : neg_inf();
-  for (int i = t; i < n; i += kThreads)
-    mx = fmaxf(mx, ml[(size_t)(slot0 + i) * Hq + h].x);
-  mx = wave_max(mx);
-  if ((t & 63) == 0) s_red[t >> 6] = mx;
-  __syncthreads();
-  float M = s_red[0];
+  const int hh = t / TPH, u = t % TPH;
+  const int h = h0 + hh;
+  const int c = u % CH, sg = u / CH;
+  const bool one_round = n <= NSG * R;
+
+  // All loads of the round are issued before any is used: indices past n
+  // are clamped to a valid slot and their terms dropped, and the prior is
+  // read whether or not it is used, so no load sits behind a branch.
+  float2 mv[R];
+  float4 av[R];
+  const float2 pml_raw = prior_ml[has_prior ? hh : 0];
+  const float pacc_raw = prior_acc[has_prior && t < NH * D ? t : 0];
+  const float2 pml = has_prior ? pml_raw : make_float2(neg_inf(), 0.f);
+  const float pacc = has_prior ? pacc_raw : 0.f;
+  float mx = pml.x;
+  if (one_round && n > 0) {
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w]);
+    for (int k = 0; k < R; ++k) {
+      const int i = min(sg + k * NSG, n - 1);
+      const size_t sl = (size_t)(slot0 + i) * Hq + h;
+      mv[k] = ml[sl];
+      av[k] = ((const float4 *)(acc + sl * D))[c];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (sg + k * NSG < n) mx = fmaxf(mx, mv[k].x);
+  } else if (!one_round) {
+    for (int i = u; i < n; i += TPH)
+      mx = fmaxf(mx, ml[(size_t)(slot0 + i) * Hq + h].x);
+  }
+#pragma unroll
+  for (int off = (TPH < 64 ? TPH : 64) / 2; off >= 1; off >>= 1)
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (TPH >= 64) {
+    if ((u & 63) == 0) s_mx[hh][u >> 6] = mx;
+  } else if (u == 0) {
+    s_mx[hh][0] = mx;
+  }
+  __syncthreads();
+  float M = s_mx[hh][0];
+#pragma unroll
+  for (int w = 1; w < WPH; ++w) M = fmaxf(M, s_mx[hh][w]);
   const float ref = exp_ref(M);
 
-  const int c = t % CH, sg = t / CH;
   float ls = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = sg; i < n; i += NSG) {
-    const size_t sl = (size_t)(slot0 + i) * Hq + h;
-    const float2 mli = ml[sl];
-    const float4 ai = ((const float4 *)(acc + sl * D))[c];
-    const float w = fast_exp2(mli.x - ref);
-    ls += mli.y * w;
-    a.x += ai.x * w;
-    a.y += ai.y * w;
-    a.z += ai.z * w;
-    a.w += ai.w * w;
+  for (int base = sg; base < n; base += NSG * R) {
+    if (!one_round) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int i = base + k * NSG;
+        if (i < n) {
+          const size_t sl = (size_t)(slot0 + i) * Hq + h;
+          mv[k] = ml[sl];
+          av[k] = ((const float4 *)(acc + sl * D))[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (base + k * NSG < n) {
+        const float w = fast_exp2(mv[k].x - ref);
+        ls += mv[k].y * w;
+        a.x += av[k].x * w;
+        a.y += av[k].y * w;
+        a.z += av[k].z * w;
+        a.w += av[k].w * w;
+      }
+    }
   }
-  s_pacc[sg][c] = a;
-  if (c == 0) s_pl[sg] = ls;
+  s_pacc[hh][sg][c] = a;
+  if (c == 0) s_pl[hh][sg] = ls;
   __syncthreads();
-  if (t < D) {
+  // thread t < NH * D owns (head t / D, element t % D) of the result
+  for (int idx = t; idx < NH * D; idx += kThreads) {
+    const int h2 = idx / D, d = idx % D;
+    float Mh = s_mx[h2][0];
+#pragma unroll
+    for (int w = 1; w < WPH; ++w) Mh = fmaxf(Mh, s_mx[h2][w]);
     float tot = 0.f;
-    if (has_prior) tot = prior_acc[t] * fast_exp2(prior_ml.x - ref);
+    if (has_prior) {
+      const float pa = (idx == t) ? pacc : prior_acc[idx];
+      tot = pa * fast_exp2(prior_ml[h2].x - exp_ref(Mh));
+    }
 #pragma unroll
-    for (int g = 0; g < NSG; ++g) tot += ((const float *)&s_pacc[g][0])[t];
-    res_acc[t] = tot;
+    for (int g = 0; g < NSG; ++g) tot += ((const float *)&s_pacc[h2][g][0])[d];
+    res_acc[idx] = tot;
   }
-  if (t == 0) {
-    float tl = has_prior ? prior_ml.y * fast_exp2(prior_ml.x - ref) : 0.f;
+  if (t < NH) {
+    float Mh = s_mx[t][0];
 #pragma unroll
-    for (int g = 0; g < NSG; ++g) tl += s_pl[g];
-    *res_l = tl;
-    *res_m = M;
+    for (int w = 1; w < WPH; ++w) Mh = fmaxf(Mh, s_mx[t][w]);
+    float tl = has_prior ? prior_ml[t].y * fast_exp2(prior_ml[t].x - exp_ref(Mh))
+                         : 0.f;
+#pragma unroll
+    for (int g = 0; g < NSG; ++g) tl += s_pl[t][g];
+    res_l[t] = tl;
+    res_m[t] = Mh;
   }
   __syncthreads();
 }
@@ -346,22 +651,26 @@ __device__ __forceinline__ float ratio_of(float num, float den) {
 }
 
 // Returns true in every thread of the block for the last block to arrive at
-// `cnt` out of `total`; that block also resets the counter to zero.  Release
-// of this block's global writes before the arrival and acquire of the
-// others' after it use device-scope fences.
+// `cnt` out of `total`; that block also resets the counter to zero.  The
+// block barrier orders all of this block's global writes before thread 0's
+// device-scope release fence and arrival; the last block's thread 0 then
+// fences again (acquire) before the barrier that lets its threads read
+// what the other blocks wrote.
 __device__ bool arrive_last(unsigned *cnt, unsigned total) {
   __shared__ int s_last;
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
+    __threadfence();
     const unsigned old = atomicAdd(cnt, 1u);
-    s_last = (old == total - 1) ? 1 : 0;
-    if (s_last) atomicExch(cnt, 0u);
+    const int last = (old == total - 1) ? 1 : 0;
+    if (last) {
+      atomicExch(cnt, 0u);
+      __threadfence();
+    }
+    s_last = last;
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
 }
 
 // ---------------------------------------------------------------- kernels ---
@@ -403,86 +712,124 @@ __device__ __forceinline__ Item decode_item(const PlanArgs &pa,
   return it;
 }
 
-template <class KV, int D, int G>
-__global__ __launch_bounds__(kThreads) void partials_kernel(
-    PlanArgs pa, bool approx_set, bool combine, const float *__restrict__ q,
-    const typename KV::elem *__restrict__ k,
-    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w,
-    float *__restrict__ o_approx, float *__restrict__ lse_approx) {
-  const Item it = decode_item(pa, approx_set, blockIdx.x);
-  const int Hq = pa.Hq;
-  const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
-  const int h0 = it.g * G;
-  split_state<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
-                        v + kv_off, it.t0, it.t1, sm_log2,
-                        w.part_ml + (size_t)it.slot * Hq + h0,
-                        w.part_acc + ((size_t)it.slot * Hq + h0) * D);
-  if (!combine) return;
+// Slots merged per thread per memory round in the merges of the sink and
+// window states (a handful of splits).
+constexpr int kMergeRoundA = 16;
+// ... and in the exact merges (many middle splits).
+constexpr int kMergeRoundM = 8;
 
-  // Last block of this (entry, kv head): merge its sink + window states.
-  const int nA = pa.nsink[it.b] + pa.nwin[it.b];
-  if (!arrive_last(w.counters + it.b * kMaxKvHeads + it.g, (unsigned)nA))
-    return;
-  __shared__ float r_acc[D];
-  __shared__ float r_m, r_l;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = h0 + hh;
-    merge_head<D>(w.part_ml, w.part_acc, pa.slot_base[it.b], nA, Hq, h, false,
-                  make_float2(0.f, 0.f), nullptr, r_acc, &r_m, &r_l);
-    const size_t bh = (size_t)it.b * Hq + h;
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-      w.stA_acc[bh * D + d] = r_acc[d];
-      o_approx[bh * D + d] = normalise(r_acc[d], r_l);
+template <class KV, int D, int G>
+__device__ __forceinline__ void split_any(const float *qg,
+                                          const typename KV::elem *kb,
+                                          const typename KV::elem *vb, int t0,
+                                          int t1, float sm_log2,
+                                          float2 *out_ml, float *out_acc) {
+  if constexpr (std::is_same<KV, KvBf16>::value && D == 128 &&
+                (G == 4 || G == 8))
+    split_state_mfma<G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
+  else
+    split_state<KV, D, G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
+}
+
+// Per-head sums of the relative L2 test over a block's G x D outputs, kept
+// in fixed order: each wave sums one head's slice of a pass, then the
+// waves of a head are added in order.
+template <int D, int G>
+__device__ void group_num_den(const float *e, const float *a, float *num,
+                              float *den) {
+  constexpr int WPH = D / 64;          // waves per head in one pass
+  constexpr int HPP = kWaves / WPH;    // heads per pass
+  constexpr int PASSES = (G + HPP - 1) / HPP;
+  __shared__ float s_n[PASSES][kWaves], s_d[PASSES][kWaves];
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int idx = p * kThreads + threadIdx.x;
+    float n = 0.f, d2 = 0.f;
+    if (idx < G * D) {
+      const float diff = a[idx] - e[idx];
+      n = diff * diff;
+      d2 = e[idx] * e[idx];
     }
-    if (threadIdx.x == 0) {
-      w.stA_ml[bh] = make_float2(r_m, r_l);
-      if (lse_approx) lse_approx[bh] = lse_nat(r_m, r_l);
+    for (int off = 32; off >= 1; off >>= 1) {
+      n += __shfl_xor(n, off);
+      d2 += __shfl_xor(d2, off);
     }
-    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+      s_n[p][wave] = n;
+      s_d[p][wave] = d2;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x, p = hh / HPP, w0 = (hh % HPP) * WPH;
+    float n = s_n[p][w0], d2 = s_d[p][w0];
+#pragma unroll
+    for (int w = 1; w < WPH; ++w) {
+      n += s_n[p][w0 + w];
+      d2 += s_d[p][w0 + w];
+    }
+    num[hh] = n;
+    den[hh] = d2;
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_verify_kernel(
-    PlanArgs pa, WsPtrs w, const float *__restrict__ o_approx,
-    float *__restrict__ o_exact, float *__restrict__ lse_exact,
-    float *__restrict__ ratio, uint8_t *__restrict__ commit,
-    float *__restrict__ o_committed, float lambda) {
-  __shared__ float r_acc[D];
-  __shared__ float r_m, r_l;
-  __shared__ float s_red[kWaves];
+// Exact output of NH consecutive query heads h0.. of entry b: the stored
+// sink+window state merged with the middle slots, normalised into o_exact
+// (and lse_exact); each head's (num, den) of the verify goes to the
+// workspace.
+template <int D, int NH>
+__device__ void exact_heads(const PlanArgs &pa, const WsPtrs &w, int b,
+                            int h0, const float *__restrict__ o_approx,
+                            float *__restrict__ o_exact,
+                            float *__restrict__ lse_exact) {
+  __shared__ float r_acc[NH * D];
+  __shared__ float r_m[NH], r_l[NH];
+  __shared__ float s_num[NH], s_den[NH];
   const int Hq = pa.Hq;
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
-  const size_t bh = (size_t)b * Hq + h;
+  const size_t bh0 = (size_t)b * Hq + h0;
   const int nA = pa.nsink[b] + pa.nwin[b];
-  merge_head<D>(w.part_ml, w.part_acc, pa.slot_base[b] + nA, pa.nmid[b], Hq,
-                h, true, w.stA_ml[bh], w.stA_acc + bh * D, r_acc, &r_m, &r_l);
-  float num = 0.f, den = 0.f;
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    const float e = normalise(r_acc[d], r_l);
-    o_exact[bh * D + d] = e;
-    const float diff = o_approx[bh * D + d] - e;
-    num += diff * diff;
-    den += e * e;
+  merge_heads<D, NH, kMergeRoundM>(w.part_ml, w.part_acc,
+                                   pa.slot_base[b] + nA, pa.nmid[b], Hq, h0,
+                                   true, w.stA_ml + bh0, w.stA_acc + bh0 * D,
+                                   r_acc, r_m, r_l);
+  for (int idx = threadIdx.x; idx < NH * D; idx += kThreads) {
+    const float e = normalise(r_acc[idx], r_l[idx / D]);
+    r_acc[idx] = e;
+    o_exact[bh0 * D + idx] = e;
   }
-  num = block_sum(num, s_red);
-  den = block_sum(den, s_red);
-  if (threadIdx.x == 0) {
-    w.headnd[bh] = make_float2(num, den);
-    if (lse_exact) lse_exact[bh] = lse_nat(r_m, r_l);
+  __syncthreads();
+  group_num_den<D, NH>(r_acc, o_approx + bh0 * D, s_num, s_den);
+  __syncthreads();
+  if (threadIdx.x < NH) {
+    const int hh = threadIdx.x;
+    w.headnd[bh0 + hh] = make_float2(s_num[hh], s_den[hh]);
+    if (lse_exact) lse_exact[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
   }
-  if (!arrive_last(w.counters + kApproxCounters + b, (unsigned)Hq)) return;
+}
 
-  // Last head of entry b: per-entry ratio over all heads, in head order.
+// Per-entry verdict once every head of entry b has stored its (num, den): ratio over all heads (summed in head order), commit flag,
+// committed output.
+template <int D>
+__device__ void finalize_entry(const PlanArgs &pa, const WsPtrs &w, int b,
+                               const float *__restrict__ o_approx,
+                               const float *__restrict__ o_exact,
+                               float *__restrict__ ratio,
+                               uint8_t *__restrict__ commit,
+                               float *__restrict__ o_committed, float lambda) {
+  __shared__ float s_red[kWaves];
   __shared__ int s_commit;
+  const int Hq = pa.Hq;
+  float n = 0.f, d2 = 0.f;
+  for (int h = threadIdx.x; h < Hq; h += kThreads) {
+    const float2 nd = w.headnd[(size_t)b * Hq + h];
+    n += nd.x;
+    d2 += nd.y;
+  }
+  n = block_sum(n, s_red);
+  d2 = block_sum(d2, s_red);
   if (threadIdx.x == 0) {
-    float tn = 0.f, td = 0.f;
-    for (int hh = 0; hh < Hq; ++hh) {
-      const float2 nd = w.headnd[(size_t)b * Hq + hh];
-      tn += nd.x;
-      td += nd.y;
-    }
-    const float rt = ratio_of(tn, td);
+    const float rt = ratio_of(n, d2);
     const int cm = rt <= lambda ? 1 : 0;
     ratio[b] = rt;
     commit[b] = (uint8_t)cm;
@@ -490,28 +837,107 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(
   }
   __syncthreads();
   if (o_committed) {
-    const float *src = s_commit ? o_approx : o_exact;
-    const size_t base = (size_t)b * Hq * D;
-    for (int i = threadIdx.x; i < Hq * D; i += kThreads)
-      o_committed[base + i] = src[base + i];
+    // float4 copy, four per thread per round, loads issued before stores
+    const float4 *src = (const float4 *)((s_commit ? o_approx : o_exact) +
+                                         (size_t)b * Hq * D);
+    float4 *dst = (float4 *)(o_committed + (size_t)b * Hq * D);
+    const int n4 = Hq * D / 4;
+    for (int base = threadIdx.x; base < n4; base += 4 * kThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = src[min(base + k * kThreads, n4 - 1)];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (base + k * kThreads < n4) dst[base + k * kThreads] = v[k];
+    }
   }
 }
 
+constexpr int kStates = kPartialsStates;
+constexpr int kApprox = kPartialsApprox;
+
+// One block per work item.  With MODE == kApprox (sink and window items),
+// the last block of each (entry, kv head) -- counted with a workspace
+// counter -- also merges that head group's sink+window states into
+// o_approx / lse_approx and the reusable merged state.
+template <class KV, int D, int G, int MODE>
+__global__ __launch_bounds__(kThreads) void partials_kernel(
+    PlanArgs pa, bool approx_set, const float *__restrict__ q,
+    const typename KV::elem *__restrict__ k,
+    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w,
+    Outs o) {
+  const bool aset = MODE == kApprox || approx_set;
+  const Item it = decode_item(pa, aset, blockIdx.x);
+  const int Hq = pa.Hq;
+  const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
+  const int h0 = it.g * G;
+  split_any<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+                      v + kv_off, it.t0, it.t1, sm_log2,
+                      w.part_ml + (size_t)it.slot * Hq + h0,
+                      w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+  if constexpr (MODE == kApprox) {
+    const int nA = pa.nsink[it.b] + pa.nwin[it.b];
+    if (!arrive_last(w.counters + it.b * kMaxKvHeads + it.g, (unsigned)nA))
+      return;
+    __shared__ float r_acc[G * D];
+    __shared__ float r_m[G], r_l[G];
+    const size_t bh0 = (size_t)it.b * Hq + h0;
+    // no prior state; the stored-state slots only serve as valid addresses
+    merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc,
+                                    pa.slot_base[it.b], nA, Hq, h0, false,
+                                    w.stA_ml + bh0, w.stA_acc + bh0 * D,
+                                    r_acc, r_m, r_l);
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int hh = idx / D;
+      w.stA_acc[bh0 * D + idx] = r_acc[idx];
+      o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
+    }
+    if (threadIdx.x < G) {
+      const int hh = threadIdx.x;
+      w.stA_ml[bh0 + hh] = make_float2(r_m[hh], r_l[hh]);
+      if (o.lse_approx) o.lse_approx[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
+    }
+  }
+}
+
+// Exact merge, verify and commit: one block per (entry, query head) merges
+// that head's stored sink+window state with its middle splits in one
+// memory round; the last head of an entry to finish issues the verdict.
 template <int D>
+__global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
+                                                                WsPtrs w,
+                                                                Outs o) {
+  const int b = blockIdx.x / pa.Hq, h = blockIdx.x % pa.Hq;
+  exact_heads<D, 1>(pa, w, b, h, o.o_approx, o.o_exact, o.lse_exact);
+  if (!arrive_last(w.counters + kUserCounters + b, (unsigned)pa.Hq)) return;
+  finalize_entry<D>(pa, w, b, o.o_approx, o.o_exact, o.ratio, o.commit,
+                    o.o_committed, o.lambda);
+}
+
+// Exact output from every split state of the plan; one block per
+// (entry, kv head) with the same merge as the sink+window combine, so with
+// an empty middle both give the same bits.
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(
     PlanArgs pa, WsPtrs w, float *__restrict__ o_exact,
     float *__restrict__ lse_exact) {
-  __shared__ float r_acc[D];
-  __shared__ float r_m, r_l;
+  __shared__ float r_acc[G * D];
+  __shared__ float r_m[G], r_l[G];
   const int Hq = pa.Hq;
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
-  const size_t bh = (size_t)b * Hq + h;
+  const int b = blockIdx.x / pa.Hkv, g = blockIdx.x % pa.Hkv;
+  const int h0 = g * G;
   const int n = pa.nsink[b] + pa.nwin[b] + pa.nmid[b];
-  merge_head<D>(w.part_ml, w.part_acc, pa.slot_base[b], n, Hq, h, false,
-                make_float2(0.f, 0.f), nullptr, r_acc, &r_m, &r_l);
-  for (int d = threadIdx.x; d < D; d += kThreads)
-    o_exact[bh * D + d] = normalise(r_acc[d], r_l);
-  if (threadIdx.x == 0 && lse_exact) lse_exact[bh] = lse_nat(r_m, r_l);
+  const size_t bh0 = (size_t)b * Hq + h0;
+  // no prior state; the stored-state slots only serve as valid addresses
+  merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc, pa.slot_base[b], n,
+                                  Hq, h0, false, w.stA_ml + bh0,
+                                  w.stA_acc + bh0 * D, r_acc, r_m, r_l);
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+    o_exact[bh0 * D + idx] = normalise(r_acc[idx], r_l[idx / D]);
+  if (threadIdx.x < G && lse_exact)
+    lse_exact[bh0 + threadIdx.x] =
+        lse_nat(r_m[threadIdx.x], r_l[threadIdx.x]);
 }
 
 __global__ __launch_bounds__(kThreads) void verify_kernel(
@@ -548,37 +974,75 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
 
 // ------------------------------------------------------------- dispatch ---
 
-template <class KV, int D>
-hipError_t partials_g(const PlanArgs &pa, bool approx_set, bool combine,
-                      const float *q, const void *k, const void *v,
-                      float sm_log2, const WsPtrs &w, float *o_approx,
-                      float *lse_approx, hipStream_t s) {
-  const int items = approx_set ? pa.itemA_pre[pa.B] : pa.itemM_pre[pa.B];
+template <class KV, int D, int G>
+hipError_t partials_kg(const PlanArgs &pa, int mode, bool approx_set,
+                       const float *q, const void *k, const void *v,
+                       float sm_log2, const WsPtrs &w, const Outs &o,
+                       hipStream_t s) {
+  const bool aset = mode == kApprox || approx_set;
+  const int items = aset ? pa.itemA_pre[pa.B] : pa.itemM_pre[pa.B];
   if (items == 0) return hipSuccess;
   using E = typename KV::elem;
   const E *kk = (const E *)k;
   const E *vv = (const E *)v;
   dim3 grid(items), block(kThreads);
+  switch (mode) {
+    case kStates:
+      hipLaunchKernelGGL((partials_kernel<KV, D, G, kStates>), grid, block, 0,
+                         s, pa, approx_set, q, kk, vv, sm_log2, w, o);
+      break;
+    case kApprox:
+      hipLaunchKernelGGL((partials_kernel<KV, D, G, kApprox>), grid, block, 0,
+                         s, pa, approx_set, q, kk, vv, sm_log2, w, o);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class KV, int D>
+hipError_t partials_g(const PlanArgs &pa, int mode, bool approx_set,
+                      const float *q, const void *k, const void *v,
+                      float sm_log2, const WsPtrs &w, const Outs &o,
+                      hipStream_t s) {
   switch (pa.G) {
     case 1:
-      hipLaunchKernelGGL((partials_kernel<KV, D, 1>), grid, block, 0, s, pa,
-                         approx_set, combine, q, kk, vv, sm_log2, w, o_approx,
-                         lse_approx);
+      return partials_kg<KV, D, 1>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                   o, s);
+    case 2:
+      return partials_kg<KV, D, 2>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                   o, s);
+    case 4:
+      return partials_kg<KV, D, 4>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                   o, s);
+    case 8:
+      return partials_kg<KV, D, 8>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                   o, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t lse_combine_d(const PlanArgs &pa, const WsPtrs &w, float *o_exact,
+                         float *lse_exact, hipStream_t s) {
+  dim3 grid(pa.B * pa.Hkv), block(kThreads);
+  switch (pa.G) {
+    case 1:
+      hipLaunchKernelGGL((lse_combine_kernel<D, 1>), grid, block, 0, s, pa, w,
+                         o_exact, lse_exact);
       break;
     case 2:
-      hipLaunchKernelGGL((partials_kernel<KV, D, 2>), grid, block, 0, s, pa,
-                         approx_set, combine, q, kk, vv, sm_log2, w, o_approx,
-                         lse_approx);
+      hipLaunchKernelGGL((lse_combine_kernel<D, 2>), grid, block, 0, s, pa, w,
+                         o_exact, lse_exact);
       break;
     case 4:
-      hipLaunchKernelGGL((partials_kernel<KV, D, 4>), grid, block, 0, s, pa,
-                         approx_set, combine, q, kk, vv, sm_log2, w, o_approx,
-                         lse_approx);
+      hipLaunchKernelGGL((lse_combine_kernel<D, 4>), grid, block, 0, s, pa, w,
+                         o_exact, lse_exact);
       break;
     case 8:
-      hipLaunchKernelGGL((partials_kernel<KV, D, 8>), grid, block, 0, s, pa,
-                         approx_set, combine, q, kk, vv, sm_log2, w, o_approx,
-                         lse_approx);
+      hipLaunchKernelGGL((lse_combine_kernel<D, 8>), grid, block, 0, s, pa, w,
+                         o_exact, lse_exact);
       break;
     default:
       return hipErrorInvalidValue;
@@ -600,52 +1064,39 @@ WsPtrs ws_ptrs(void *ws, const Workspace &wl) {
   return w;
 }
 
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
-                           bool combine, const float *q, const void *k,
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, int mode,
+                           bool approx_set, const float *q, const void *k,
                            const void *v, float sm_log2, const WsPtrs &w,
-                           float *o_approx, float *lse_approx, hipStream_t s) {
+                           const Outs &o, hipStream_t s) {
   if (kv_dtype == ALSPEC_KV_BF16) {
     if (pa.D == 128)
-      return partials_g<KvBf16, 128>(pa, approx_set, combine, q, k, v,
-                                     sm_log2, w, o_approx, lse_approx, s);
-    return partials_g<KvBf16, 64>(pa, approx_set, combine, q, k, v, sm_log2,
-                                  w, o_approx, lse_approx, s);
+      return partials_g<KvBf16, 128>(pa, mode, approx_set, q, k, v, sm_log2,
+                                     w, o, s);
+    return partials_g<KvBf16, 64>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                  o, s);
   }
   if (pa.D == 128)
-    return partials_g<KvF32, 128>(pa, approx_set, combine, q, k, v, sm_log2,
-                                  w, o_approx, lse_approx, s);
-  return partials_g<KvF32, 64>(pa, approx_set, combine, q, k, v, sm_log2, w,
-                               o_approx, lse_approx, s);
+    return partials_g<KvF32, 128>(pa, mode, approx_set, q, k, v, sm_log2, w,
+                                  o, s);
+  return partials_g<KvF32, 64>(pa, mode, approx_set, q, k, v, sm_log2, w, o,
+                               s);
 }
 
 hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
-                               const float *o_approx, float *o_exact,
-                               float *lse_exact, float *ratio, uint8_t *commit,
-                               float *o_committed, float lambda,
-                               hipStream_t s) {
+                               const Outs &o, hipStream_t s) {
   dim3 grid(pa.B * pa.Hq), block(kThreads);
   if (pa.D == 128)
-    hipLaunchKernelGGL(merge_verify_kernel<128>, grid, block, 0, s, pa, w,
-                       o_approx, o_exact, lse_exact, ratio, commit,
-                       o_committed, lambda);
+    hipLaunchKernelGGL(merge_verify_kernel<128>, grid, block, 0, s, pa, w, o);
   else
-    hipLaunchKernelGGL(merge_verify_kernel<64>, grid, block, 0, s, pa, w,
-                       o_approx, o_exact, lse_exact, ratio, commit,
-                       o_committed, lambda);
+    hipLaunchKernelGGL(merge_verify_kernel<64>, grid, block, 0, s, pa, w, o);
   return hipGetLastError();
 }
 
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
                               float *o_exact, float *lse_exact,
                               hipStream_t s) {
-  dim3 grid(pa.B * pa.Hq), block(kThreads);
-  if (pa.D == 128)
-    hipLaunchKernelGGL(lse_combine_kernel<128>, grid, block, 0, s, pa, w,
-                       o_exact, lse_exact);
-  else
-    hipLaunchKernelGGL(lse_combine_kernel<64>, grid, block, 0, s, pa, w,
-                       o_exact, lse_exact);
-  return hipGetLastError();
+  if (pa.D == 128) return lse_combine_d<128>(pa, w, o_exact, lse_exact, s);
+  return lse_combine_d<64>(pa, w, o_exact, lse_exact, s);
 }
 
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,

@@ -18,6 +18,13 @@ int pow2_floor(int x) {
   return r;
 }
 
+// Power of two nearest to x (ties up).
+int pow2_near(int64_t x) {
+  int r = 1;
+  while ((int64_t)r * 2 <= x) r *= 2;
+  return (x - r >= (int64_t)2 * r - x) ? 2 * r : r;
+}
+
 }  // namespace
 
 alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
@@ -37,6 +44,7 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     return ALSPEC_ERR_INVALID_ARG;
   if (p->split_tokens < 0 || p->window_split_tokens < 0)
     return ALSPEC_ERR_INVALID_ARG;
+  if (p->overlap != 0 && p->overlap != 1) return ALSPEC_ERR_INVALID_ARG;
   for (int b = 0; b < B && b < kMaxBatch; ++b)
     if (p->seq_lens[b] < 1 || p->seq_lens[b] > p->kv_capacity)
       return ALSPEC_ERR_INVALID_ARG;
@@ -68,22 +76,22 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     if (L - (int)wb > max_win) max_win = L - (int)wb;
   }
 
-  // Middle split length: enough work items to cover the CUs several times
-  // over, but splits long enough that the per-split state stays a small
-  // share of the bytes read.
+  // Middle split length: about two work items per CU, so one wave of
+  // resident blocks covers the whole pass (no tail), with long splits whose
+  // per-split state is a small share of the bytes and whose merge is short.
   int T = p->split_tokens;
   if (T == 0) {
-    const int64_t target_items = (int64_t)4 * kNominalCUs;
-    int64_t t = mid_tokens / (target_items > 0 ? target_items : 1);
+    const int64_t target_items = (int64_t)2 * kNominalCUs;
+    int64_t t = mid_tokens / target_items;
     if (t < 256) t = 256;
-    if (t > 4096) t = 4096;
-    T = pow2_floor((int)t);
+    if (t > 8192) t = 8192;
+    T = pow2_near(t);
   }
   // Window split length: the window is on the approximation's latency path,
-  // so it is cut finer (about 16 splits for a window of 2048).
+  // so it is cut into about 8 pieces that run side by side.
   int Tw = p->window_split_tokens;
   if (Tw == 0) {
-    Tw = max_win / 16;
+    Tw = max_win / 8;
     if (Tw < 64) Tw = 64;
     if (Tw > 512) Tw = 512;
     Tw = pow2_floor(Tw);

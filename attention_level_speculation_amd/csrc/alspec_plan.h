@@ -15,11 +15,11 @@ constexpr int kMaxKvHeads = ALSPEC_MAX_KV_HEADS;
 constexpr size_t kWsAlign = 256;
 // counters at the start of every workspace, independent of the shape, so a
 // workspace reused for another shape still finds them at zero:
-//   [0, kMaxBatch*kMaxKvHeads)          approximation merge, per (b, g)
-//   [kApproxCounters, + kMaxBatch)      verify, per b
-constexpr int kApproxCounters = kMaxBatch * kMaxKvHeads;
-constexpr int kNumCounters = kApproxCounters + kMaxBatch;
-constexpr size_t kCounterBytes = 32768;
+//   [0, kUserCounters)                 sink+window merge, per (b, g)
+//   [kUserCounters, + kMaxBatch)       heads done (exact merge), per b
+constexpr int kUserCounters = kMaxBatch * kMaxKvHeads;
+constexpr int kNumCounters = kUserCounters + kMaxBatch;
+constexpr size_t kCounterBytes = 65536;
 static_assert(kNumCounters * 4 <= (int)kCounterBytes, "counter region");
 
 // Everything a kernel needs to map a block index to its work; passed by

@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative flash-decode step of attention-level
+speculation (ALSpec) on one MI355X.
+
+Workload (the headline long-context case): one user's decode token through
+32 layers of Llama-3-8B-shaped attention -- 32 query heads over 8 kv heads,
+head dim 128, bf16 KV with fp32 arithmetic, context 131072 (512 MiB of KV
+per layer), sink 4, window 2048, lambda 0.10 -- for needle densities
+0, 1, 2, 4, 8 and 16 per kv head.  All 6 x 32 layers (96 GiB) are drawn on
+the device by the seeded generator and stay resident; a step is one token
+through the 32 layers of one density (densities rotate step by step), each
+layer one fused call of the library (approximation on one stream, exact
+split-K pass, merge and verify on another).
+
+Reported: tokens*layers/s (whole-job throughput, inputs resident in HBM),
+KV GB/s of the exact split-K kernel against the HBM peak (HIP events
+around every launch, on the stream it runs on), the speculation hit rate per
+density, the approximation's and the exact path's latency per layer and the
+critical-path time a commit saves, the HBM probe, and the CPU oracle timed
+on a bounded sample of the same layers.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("spec flash-decode tokens·layers/s + KV GB/s (% HBM peak) at "
+          "128K; hit rate")
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=120)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--densities", default="0,1,2,4,8,16")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--window-split-tokens", type=int, default=0)
+    ap.add_argument("--overlap", type=int, default=0,
+                    help="1: start the exact pass together with the "
+                         "approximation instead of after it")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run approximation and exact pass on one stream")
+    ap.add_argument("--no-events", action="store_true",
+                    help="time without per-launch events (no roofline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-probe", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (world size "
+              f"{world}) is not supported: this path has no multi-GPU "
+              "sharding (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_level_speculation_amd as al
+    from attention_level_speculation_amd import _binding as B_
+    from synth import device as sdev
+    from synth import gen
+
+    dens = [int(x) for x in args.densities.split(",")]
+    nl = args.layers
+    works = [gen.llama8b_128k(needles=n) for n in dens]
+    w0 = works[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs resident in HBM --------------------------------------
+    t0 = time.time()
+    Ks, Vs, Qs = [], [], []
+    for di, w in enumerate(works):
+        K = torch.empty((nl, w.B, w.Hkv, w.L_cap, w.D), dtype=torch.bfloat16,
+                        device=dev)
+        V = torch.empty_like(K)
+        Q = torch.empty((nl, w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+        for layer in range(nl):
+            sdev.fill_kv(w, layer, K[layer], V[layer])
+            Q[layer].copy_(torch.from_numpy(gen.q_all(w, layer)))
+        torch.cuda.synchronize()
+        Ks.append(K)
+        Vs.append(V)
+        Qs.append(Q)
+        log(f"drew needles={dens[di]}: {nl} layers "
+            f"({2 * K.numel() * 2 / 2**30:.1f} GiB) t={time.time() - t0:.1f}s")
+
+    p = al.params_for(w0, split_tokens=args.split_tokens,
+                      window_split_tokens=args.window_split_tokens,
+                      overlap=args.overlap)
+    splits, (T, Tw) = al.plan_splits(p, 0)
+    n_mid = sum(1 for s in splits if s[0] == 2)
+    mid_tokens = sum(e - b for k, b, e in splits if k == 2)
+    a_tokens = sum(e - b for k, b, e in splits if k != 2)
+    bytes_per_token = w0.Hkv * w0.D * 2 * 2           # K and V, bf16
+    mid_bytes = mid_tokens * bytes_per_token * w0.B   # one exact launch
+    layer_bytes = sum(w0.seq_lens) * bytes_per_token  # every KV byte
+    h = al.Handle(0)
+    ws = al.alloc_workspace(p, dev)
+    outs = [[al.alloc_outputs(p, dev) for _ in range(nl)] for _ in dens]
+    sa = torch.cuda.Stream(device=dev)
+    se = sa if args.one_stream else torch.cuda.Stream(device=dev)
+
+    # pre-marshalled C-ABI arguments of every (density, layer) call
+    def call_args(di, layer):
+        o = outs[di][layer]
+        return [h.ptr, ctypes.byref(p), Qs[di][layer].data_ptr(),
+                Ks[di][layer].data_ptr(), Vs[di][layer].data_ptr(),
+                o["o_approx"].data_ptr(), o["lse_approx"].data_ptr(),
+                o["o_exact"].data_ptr(), o["lse_exact"].data_ptr(),
+                o["ratio"].data_ptr(), o["commit"].data_ptr(),
+                o["o_committed"].data_ptr(), ws.data_ptr(), ws.numel(),
+                sa.cuda_stream, se.cuda_stream]
+    ARGS = [[call_args(di, layer) for layer in range(nl)]
+            for di in range(len(dens))]
+    fn = B_._spec_decode
+
+    def run_step(step, evsets=None):
+        di = step % len(dens)
+        for layer in range(nl):
+            ev = None
+            if evsets is not None:
+                ev = ctypes.byref(evsets[step][layer][0])
+            st = fn(*ARGS[di][layer], ev)
+            if st != 0:
+                raise al.AlspecError(st, "alspec_spec_decode")
+
+    # ---- warmup and timed region --------------------------------------
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    evsets = None
+    if not args.no_events:
+        names = ("approx_begin", "approx_end", "exact_begin", "exact_end",
+                 "verify_end")
+        evsets = []
+        for s in range(args.steps):
+            row = []
+            for layer in range(nl):
+                evs = {n: torch.cuda.Event(enable_timing=True) for n in names}
+                for ev_ in evs.values():
+                    ev_.record(se)   # torch creates the hipEvent lazily
+                st = B_.Events(*[evs[n].cuda_event for n in names])
+                row.append((st, evs))
+            evsets.append(row)
+    log(f"timed region: {args.steps} steps x {nl} layers, split {T} "
+        f"(middle splits {n_mid}), window split {Tw}")
+    torch.cuda.synchronize()          # barrier: one rank
+    ref_ev = torch.cuda.Event(enable_timing=True)
+    ref_ev.record(se)
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        run_step(s, evsets)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall = t_end - t_start
+    ms_per_step = wall / args.steps * 1e3
+    tok_layers_per_s = w0.B * nl * args.steps / wall
+
+    # ---- per-launch timings -------------------------------------------
+    # every event is read against one reference event recorded before the
+    # timed region, so times on the two streams share one origin
+    res = {}
+    if evsets is not None:
+        def at(ev):
+            return ref_ev.elapsed_time(ev) * 1e3   # microseconds
+        ex, t_ap, t_ex, saved, tot = [], [], [], 0.0, 0.0
+        for s_ in range(args.steps):
+            di = s_ % len(dens)
+            for layer in range(nl):
+                e = evsets[s_][layer][1]
+                a0, a1 = at(e["approx_begin"]), at(e["approx_end"])
+                e0, e1 = at(e["exact_begin"]), at(e["exact_end"])
+                v1 = at(e["verify_end"])
+                start = min(a0, e0)
+                ex.append(e1 - e0)
+                t_ap.append(a1 - start)
+                t_ex.append(v1 - start)
+                if int(outs[di][layer]["commit"][0].item()):
+                    saved += max(0.0, v1 - a1)
+                tot += v1 - start
+        ex = np.array(ex)
+        res = {
+            "exact_kernel_us_mean": float(ex.mean()),
+            "exact_kernel_us_p10": float(np.percentile(ex, 10)),
+            "exact_kernel_us_p90": float(np.percentile(ex, 90)),
+            "approx_ready_us_mean": float(np.mean(t_ap)),
+            "exact_ready_us_mean": float(np.mean(t_ex)),
+            "critical_path_saved_frac": saved / tot if tot > 0 else 0.0,
+        }
+        res["approx_over_exact"] = (res["approx_ready_us_mean"] /
+                                    res["exact_ready_us_mean"])
+
+    # ---- hit rate -------------------------------------------------------
+    hits = {}
+    allc = []
+    for di, n in enumerate(dens):
+        c = [int(outs[di][layer]["commit"][0].item()) for layer in range(nl)]
+        hits[str(n)] = sum(c) / len(c)
+        allc += c
+    hit_rate = sum(allc) / len(allc)
+
+    out = {
+        "metric": METRIC,
+        "value": tok_layers_per_s,
+        "unit": "tokens·layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded Philox generator, planted sink and "
+                "needles; no datasets, no weights",
+        "config": {
+            "workload": "llama3-8b-shaped decode attention, context 131072, "
+                        "batch 1, 32 q / 8 kv heads, head dim 128, bf16 KV, "
+                        f"{nl} layers, sink 4, window 2048, lambda 0.10, "
+                        f"needles per kv head {dens}",
+            "kv_dtype": "bf16", "arith": "f32", "context": w0.L_cap,
+            "batch": w0.B, "layers": nl, "num_q_heads": w0.Hq,
+            "num_kv_heads": w0.Hkv, "head_dim": w0.D, "sink": w0.S,
+            "window": w0.W, "lambda": w0.lam, "split_tokens": T,
+            "window_split_tokens": Tw, "middle_splits_per_head": n_mid,
+            "streams": 1 if args.one_stream else 2,
+            "overlap": args.overlap,
+            "generator": {"a": w0.const.a, "c_s": w0.const.c_s,
+                          "tau_s": w0.const.tau_s, "c_n": w0.const.c_n,
+                          "tau_n": w0.const.tau_n},
+        },
+        "hit_rate": hit_rate,
+        "hit_rate_by_needles": hits,
+        "kv_bytes_per_layer": layer_bytes,
+        "step_kv_GBps": layer_bytes * nl * args.steps / wall / 1e9,
+    }
+    out["step_hbm_frac"] = out["step_kv_GBps"] / HBM_PEAK_GBPS
+    out.update(res)
+    if res:
+        achieved = mid_bytes / (res["exact_kernel_us_mean"] * 1e-6) / 1e9
+        out["roofline"] = {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "kernel": "partials_kernel<KvBf16,128,4> (middle splits)",
+            "algorithmic_bytes_per_launch": mid_bytes,
+            "approx_tokens_per_head": a_tokens,
+        }
+
+    # ---- CPU oracle baseline --------------------------------------------
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, works, dens, outs, nl, Qs,
+                                           Ks, Vs)
+
+    # ---- HBM probe ----------------------------------------------------------
+    if not args.no_probe:
+        del Ks, Vs
+        ARGS = None
+        torch.cuda.empty_cache()
+        pr = sdev.probe_bandwidth()
+        out["probe"] = {k: round(v["GBps"], 1) for k, v in pr.items()}
+        if "roofline" in out:
+            out["roofline"]["frac_of_probe_read"] = (
+                out["roofline"]["achieved"] / pr["read"]["GBps"])
+
+    print(json.dumps(out), flush=True)
+    h.close()
+
+
+def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
+    """The oracle as it stands, on all host cores, on a bounded sample of
+    the same layers: whole layers, copied from the device-resident inputs
+    (the generator's device twin, equal to its host definition)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = oracle.default_threads()
+    secs = 0.0
+    n = 0
+    agree = 0
+    order = [(di, layer) for layer in range(nl) for di in range(len(dens))]
+    for di, layer in order:
+        w = works[di]
+        q = Qs[di][layer].cpu().numpy()
+        k = Ks[di][layer].view(torch.int16).cpu().numpy().view(np.uint16)
+        v = Vs[di][layer].view(torch.int16).cpu().numpy().view(np.uint16)
+        t = time.perf_counter()
+        r = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam,
+                               threads=threads)
+        secs += time.perf_counter() - t
+        n += 1
+        g = int(outs[di][layer]["commit"][0].item())
+        agree += int(g == int(r["commit"][0]) or
+                     abs(r["ratio"][0] - w.lam) <= 1e-4)
+        if secs >= args.cpu_seconds:
+            break
+    return {"value": n * works[0].B / secs, "unit": "tokens·layers/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{n} of the {len(dens) * nl} (needles, layer) pairs "
+                      "of the same workload: whole layers (32 heads, context "
+                      "131072), double precision, about "
+                      f"{args.cpu_seconds:.0f} s of oracle time",
+            "seconds": secs, "sample_flags_agree": f"{agree}/{n}"}
+
+
+if __name__ == "__main__":
+    main()

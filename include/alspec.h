@@ -32,6 +32,7 @@
  *      lse_*         : float32 [B][Hq] (natural log of the softmax
  *                      normaliser, logits included)
  *      ratio         : float32 [B];  commit : uint8 [B] (1 = commit)
+ *    q, k, v and the o_* arrays must be 16-byte aligned.
  *  - The caller owns every buffer and stream.  The library allocates no
  *    device memory and keeps no pointer after a call returns.
  *  - Compute calls only enqueue work on the given stream(s); they do not
@@ -83,6 +84,9 @@ typedef struct {
   float lambda;         /* verify threshold, >= 0 (+inf allowed, NaN not) */
   int32_t split_tokens;        /* middle split length; 0 = automatic */
   int32_t window_split_tokens; /* window split length; 0 = automatic */
+  int32_t overlap; /* fused call only: 0 = the exact pass starts once the
+                      approximation is done (it then has the GPU to itself
+                      and is ready soonest); 1 = both start together */
 } alspec_params;
 
 #define ALSPEC_MAX_BATCH 64
@@ -183,16 +187,23 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
 /*
  * The whole speculative step (atlas.scime.ai summary, Approach; ICML poster
  * abstract: the approximation lets later work start early while exact
- * attention runs, then a verify commits or discards).  On stream_approx:
- * the sink and window splits and their merge, producing o_approx (and
- * lse_approx if non-NULL); work enqueued on stream_approx after this call
- * may consume o_approx.  On stream_exact: the middle splits, then (after
- * the approximation's work) the merge with the reused sink/window state
- * into o_exact (and lse_exact if non-NULL), the relative L2 verify into
- * ratio and commit, and, if non-NULL, o_committed.  The call first orders
- * stream_approx after the work already enqueued on stream_exact, so
- * successive calls on the same workspace are safe.  The two streams may be
- * the same stream.  `ev` may be NULL.
+ * attention runs, then a verify commits or discards).  Writes o_approx
+ * (and lse_approx if non-NULL), o_exact (and lse_exact if non-NULL), the
+ * per-entry ratio and commit flag and, if non-NULL, o_committed.
+ *
+ * With p->overlap == 0 (default) every kernel runs on stream_exact: the
+ * sink and window splits and their merge (o_approx), then the middle
+ * splits, then the merge with the reused sink/window state, the verify and
+ * the commit.  stream_approx is made to wait for the approximation only,
+ * so work enqueued on stream_approx after this call may consume o_approx
+ * while the exact pass runs.  With p->overlap == 1 the approximation runs
+ * on stream_approx while the middle splits start on stream_exact; the
+ * exact merge and verify then wait for both (stream_approx is first
+ * ordered after the work already queued on stream_exact, so successive
+ * calls on one workspace are safe).  Results are identical in both modes.
+ * The two streams may be the same stream.  `ev` may be NULL.  Buffers
+ * written by a call must not be read by the caller's own work until it is
+ * ordered after the call's completion on the stream named above.
  */
 alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  const float *q, const void *k, const void *v,

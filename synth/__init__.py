@@ -1,2 +1,3 @@
 """Seeded synthetic inputs shared by the oracle's and the GPU library's tests
-and by the benchmark.  Draws numbers only; holds no attention arithmetic."""
+and by the benchmark, plus the benchmark's HBM bandwidth probes.  Holds no
+attention arithmetic."""

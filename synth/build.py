@@ -1,9 +1,11 @@
-"""Build the device half of the input generator (libalspec_synth.so)."""
+"""Build libalspec_synth.so: the device half of the input generator and the
+bandwidth probes the benchmark uses."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "synth_kernels.hip")
+SRCS = [os.path.join(HERE, "synth_kernels.hip"),
+        os.path.join(HERE, "probe_kernels.hip")]
 LIB = os.path.join(HERE, "libalspec_synth.so")
 
 
@@ -11,7 +13,7 @@ def build(verbose: bool = False) -> str:
     cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
            "-shared", "-ffp-contract=off",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-o", LIB + ".tmp", SRC]
+           "-o", LIB + ".tmp"] + SRCS
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

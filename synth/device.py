@@ -78,3 +78,55 @@ def layer_to_device(w: gen.Workload, layer: int, device="cuda"):
     fill_kv(w, layer, k, v)
     q = torch.from_numpy(gen.q_all(w, layer)).to(device)
     return q, k, v
+
+
+def _probe_lib():
+    lib = _load()
+    if not hasattr(lib, "_probe_sig"):
+        lib.probe_read.restype = ctypes.c_int
+        lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+        lib.probe_copy.restype = ctypes.c_int
+        lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+        lib._probe_sig = True
+    return lib
+
+
+def probe_bandwidth(nbytes=4 << 30, reps=10, blocks=256 * 16):
+    """Achievable read and copy bandwidth (GB/s, 1e9 bytes) over `nbytes`
+    buffers, timed with HIP events; each kernel averaged over `reps`."""
+    import torch
+    lib = _probe_lib()
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    res = {}
+    for name in ("read", "copy"):
+        def launch():
+            if name == "read":
+                rc = lib.probe_read(src.data_ptr(), nbytes, sink.data_ptr(),
+                                    blocks, s.cuda_stream)
+            else:
+                rc = lib.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                    blocks, s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe_{name} failed: {rc}")
+        launch()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            launch()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        moved = nbytes * (1 if name == "read" else 2)
+        res[name] = {"bytes_per_launch": moved, "ms": ms,
+                     "GBps": moved / (ms * 1e-3) / 1e9}
+    del src, dst, sink
+    return res

@@ -211,9 +211,12 @@ def test_determinism_and_one_vs_two_streams(handle):
     a = run_fused(al, handle, p, *dev, two_streams=True)
     b = run_fused(al, handle, p, *dev, two_streams=True)
     c = run_fused(al, handle, p, *dev, two_streams=False)
+    d = run_fused(al, handle, al.params_for(w, overlap=1), *dev,
+                  two_streams=True)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
         assert np.array_equal(a[key], c[key]), key
+        assert np.array_equal(a[key], d[key]), key
 
 
 def test_back_to_back_calls_share_workspace(handle):
