@@ -7,12 +7,15 @@ Python binding over it.  Importing fails if the library is not built.
 """
 from ._binding import (AlspecError, Events, Handle, KV_BF16, KV_F32,
                        LIB_PATH, Params, alloc_outputs, alloc_workspace,
-                       flash_decode_exact, lse_combine, make_params,
-                       params_for, plan_splits, sink_approx, spec_decode,
-                       status_string, verify, version, workspace_size)
+                       flash_decode_exact, last_error, lse_combine,
+                       make_params,
+                       order_after_verify, params_for, plan_splits,
+                       sink_approx, spec_decode, status_string, verify,
+                       version, workspace_size)
 
 __all__ = ["AlspecError", "Events", "Handle", "KV_BF16", "KV_F32",
            "LIB_PATH", "Params", "alloc_outputs", "alloc_workspace",
-           "flash_decode_exact", "lse_combine", "make_params", "params_for",
+           "flash_decode_exact", "last_error", "lse_combine", "make_params",
+           "order_after_verify", "params_for",
            "plan_splits", "sink_approx", "spec_decode", "status_string",
            "verify", "version", "workspace_size"]

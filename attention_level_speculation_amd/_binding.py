@@ -63,6 +63,9 @@ _PP = ctypes.POINTER(Params)
 _status_string = getattr(_lib, "alspec_status_string")
 _status_string.restype = ctypes.c_char_p
 _status_string.argtypes = [ctypes.c_int]
+_last_error = getattr(_lib, "alspec_last_error")
+_last_error.restype = ctypes.c_char_p
+_last_error.argtypes = []
 _version = getattr(_lib, "alspec_version")
 _version.restype = _i32
 _workspace_size = _sig("alspec_workspace_size", _PP,
@@ -79,6 +82,7 @@ _flash_exact = _sig("alspec_flash_decode_exact", _P, _PP, _P, _P, _P, _i32,
 _lse_combine = _sig("alspec_lse_combine", _P, _PP, _P, ctypes.c_size_t, _P,
                     _P, _P)
 _verify = _sig("alspec_verify", _P, _PP, _P, _P, _P, _P, _P, _P)
+_order_after_verify = _sig("alspec_order_after_verify", _P, _P)
 _spec_decode = _sig("alspec_spec_decode", _P, _PP, _P, _P, _P, _P, _P, _P,
                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
                     ctypes.POINTER(Events))
@@ -87,7 +91,15 @@ _spec_decode = _sig("alspec_spec_decode", _P, _PP, _P, _P, _P, _P, _P, _P,
 class AlspecError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
-        super().__init__(f"{what}: {status_string(status)}")
+        msg = f"{what}: {status_string(status)}"
+        if int(status) == 4:               # ALSPEC_ERR_HIP
+            msg += f" ({last_error()})"
+        super().__init__(msg)
+
+
+def last_error():
+    """The HIP call and error behind this thread's last ALSPEC_ERR_HIP."""
+    return _last_error().decode()
 
 
 def status_string(st):
@@ -338,3 +350,10 @@ def spec_decode(h, p, q, k, v, out, ws, stream_approx=None,
              "o_committed", True),
         wp, wn, sa, se, ctypes.byref(ev) if ev is not None else None),
         "alspec_spec_decode")
+
+
+def order_after_verify(h, stream=None):
+    """Order `stream` (default: current) after the merge/verify work that
+    pipelined calls on handle `h` have enqueued."""
+    _check(_order_after_verify(h.ptr, _stream(stream)),
+           "alspec_order_after_verify")

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -10,10 +11,35 @@
 #include "alspec_kernels.h"
 #include "alspec_plan.h"
 
+// Fused calls remember, per workspace, the event that follows the last
+// verify reading it, so that a later call on that workspace in another
+// stream waits for it.
+constexpr int kWsTable = 16;
+
+struct WsEntry {
+  const void *ws;
+  hipEvent_t ev;
+  hipStream_t stream;  // stream `ev` was recorded on
+  uint64_t tick;
+  bool used;
+};
+
+// Whether `s` is capturing into a graph.
+static bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &status) == hipSuccess &&
+         status == hipStreamCaptureStatusActive;
+}
+
 struct alspec_handle {
   int device;
+  hipStream_t sv;        // verify stream of pipelined calls
   hipEvent_t ev_join;    // exact stream -> approximation stream
-  hipEvent_t ev_approx;  // approximation stream -> exact stream
+  hipEvent_t ev_approx;  // approximation done
+  hipEvent_t ev_mid;     // middle splits done (pipelined calls)
+  hipEvent_t ev_verify;  // verify stream tail (alspec_order_after_verify)
+  WsEntry ws_table[kWsTable];
+  uint64_t tick;
 };
 
 namespace {
@@ -22,8 +48,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-alspec_status hip_status(hipError_t e) {
-  return e == hipSuccess ? ALSPEC_OK : ALSPEC_ERR_HIP;
+// Description of the last HIP failure on this thread (alspec_last_error).
+thread_local char g_last_error[200];
+
+// True when e is an error; the failing call is then noted for
+// alspec_last_error.
+bool failed(hipError_t e, const char *what) {
+  if (e == hipSuccess) return false;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what,
+           hipGetErrorName(e), (int)e);
+  return true;
+}
+
+alspec_status hip_status(hipError_t e, const char *what) {
+  return failed(e, what) ? ALSPEC_ERR_HIP : ALSPEC_OK;
 }
 
 // Common checks of the q/k/v pointers and the workspace.
@@ -36,7 +74,8 @@ alspec_status check_inputs(const float *q, const void *k, const void *v) {
 
 // Output arrays are written with 16-byte vector stores.
 alspec_status check_outputs(const float *a, const float *b, const float *c) {
-  if ((a && !aligned(a, 16)) || (b && !aligned(b, 16)) || (c && !aligned(c, 16)))
+  if ((a && !aligned(a, 16)) || (b && !aligned(b, 16)) ||
+      (c && !aligned(c, 16)))
     return ALSPEC_ERR_INVALID_ARG;
   return ALSPEC_OK;
 }
@@ -49,9 +88,31 @@ alspec_status check_ws(const void *ws, size_t ws_bytes,
   return ALSPEC_OK;
 }
 
+// Entry of the workspace table for `ws`: its own entry if the table has
+// one, else (*fresh = true) a free entry or the least recently used one,
+// whose old event the caller still has to honour.
+WsEntry *ws_entry(alspec_handle *h, const void *ws, bool *fresh) {
+  *fresh = false;
+  for (int i = 0; i < kWsTable; ++i)
+    if (h->ws_table[i].used && h->ws_table[i].ws == ws) return &h->ws_table[i];
+  *fresh = true;
+  for (int i = 0; i < kWsTable; ++i)
+    if (!h->ws_table[i].used) return &h->ws_table[i];
+  WsEntry *e = &h->ws_table[0];
+  for (int i = 1; i < kWsTable; ++i)
+    if (h->ws_table[i].tick < e->tick) e = &h->ws_table[i];
+  return e;
+}
+
+// Caller's timing events; inside a stream capture they become event nodes
+// that take their timestamps when the graph runs.
 alspec_status record(void *ev, hipStream_t s) {
   if (!ev) return ALSPEC_OK;
-  return hip_status(hipEventRecord((hipEvent_t)ev, s));
+  if (capturing(s))
+    return hip_status(
+        hipEventRecordWithFlags((hipEvent_t)ev, s, hipEventRecordExternal),
+        "hipEventRecordWithFlags");
+  return hip_status(hipEventRecord((hipEvent_t)ev, s), "hipEventRecord");
 }
 
 }  // namespace
@@ -70,6 +131,8 @@ const char *alspec_status_string(alspec_status s) {
 }
 
 int32_t alspec_version(void) { return 100; }
+
+const char *alspec_last_error(void) { return g_last_error; }
 
 alspec_status alspec_workspace_size(const alspec_params *p, size_t *bytes) {
   if (!p || !bytes) return ALSPEC_ERR_INVALID_ARG;
@@ -121,23 +184,29 @@ alspec_status alspec_create(int device, alspec_handle **out) {
   if (!out) return ALSPEC_ERR_INVALID_ARG;
   *out = nullptr;
   int n = 0;
-  if (hipGetDeviceCount(&n) != hipSuccess) return ALSPEC_ERR_HIP;
+  if (failed(hipGetDeviceCount(&n), "hipGetDeviceCount"))
+    return ALSPEC_ERR_HIP;
   if (device < 0 || device >= n) return ALSPEC_ERR_INVALID_ARG;
   int prev = 0;
-  if (hipGetDevice(&prev) != hipSuccess) return ALSPEC_ERR_HIP;
-  if (hipSetDevice(device) != hipSuccess) return ALSPEC_ERR_HIP;
+  if (failed(hipGetDevice(&prev), "hipGetDevice")) return ALSPEC_ERR_HIP;
+  if (failed(hipSetDevice(device), "hipSetDevice")) return ALSPEC_ERR_HIP;
   alspec_handle *h = (alspec_handle *)calloc(1, sizeof(alspec_handle));
   alspec_status st = ALSPEC_OK;
   if (!h) {
     st = ALSPEC_ERR_INVALID_ARG;
   } else {
     h->device = device;
-    if (hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) !=
-            hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_approx, hipEventDisableTiming) !=
-            hipSuccess) {
-      if (h->ev_join) (void)hipEventDestroy(h->ev_join);
-      free(h);
+    auto event = [](hipEvent_t *e) {
+      return !failed(hipEventCreateWithFlags(e, hipEventDisableTiming),
+                     "hipEventCreateWithFlags");
+    };
+    bool ok = event(&h->ev_join) && event(&h->ev_approx) &&
+              event(&h->ev_mid) && event(&h->ev_verify) &&
+              !failed(hipStreamCreateWithFlags(&h->sv, hipStreamNonBlocking),
+                      "hipStreamCreateWithFlags");
+    for (int i = 0; ok && i < kWsTable; ++i) ok = event(&h->ws_table[i].ev);
+    if (!ok) {
+      alspec_destroy(h);
       h = nullptr;
       st = ALSPEC_ERR_HIP;
     }
@@ -151,6 +220,11 @@ alspec_status alspec_destroy(alspec_handle *h) {
   if (!h) return ALSPEC_ERR_INVALID_ARG;
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_approx) (void)hipEventDestroy(h->ev_approx);
+  if (h->ev_mid) (void)hipEventDestroy(h->ev_mid);
+  if (h->ev_verify) (void)hipEventDestroy(h->ev_verify);
+  if (h->sv) (void)hipStreamDestroy(h->sv);
+  for (int i = 0; i < kWsTable; ++i)
+    if (h->ws_table[i].ev) (void)hipEventDestroy(h->ws_table[i].ev);
   free(h);
   return ALSPEC_OK;
 }
@@ -170,9 +244,12 @@ alspec_status alspec_sink_approx(alspec_handle *h, const alspec_params *p,
   alspec::Outs o{};
   o.o_approx = o_approx;
   o.lse_approx = lse_approx;
-  return hip_status(alspec::launch_partials(
-      pa, p->kv_dtype, alspec::kPartialsApprox, true, q, k, v,
-      p->sm_scale * kLog2e, w, o, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
+                              p->sm_scale * kLog2e, w, s), "launch_partials"))
+    return ALSPEC_ERR_HIP;
+  return hip_status(alspec::launch_approx_combine(pa, w, o, s),
+                    "launch_approx_combine");
 }
 
 alspec_status alspec_flash_decode_exact(alspec_handle *h,
@@ -193,16 +270,14 @@ alspec_status alspec_flash_decode_exact(alspec_handle *h,
   const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
   const float sm_log2 = p->sm_scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
-  const alspec::Outs none{};
-  if (include_sink_window) {
-    hipError_t e =
-        alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates,
-                                true, q, k, v, sm_log2, w, none, s);
-    if (e != hipSuccess) return ALSPEC_ERR_HIP;
-  }
-  return hip_status(alspec::launch_partials(pa, p->kv_dtype,
-                                            alspec::kPartialsStates, false, q,
-                                            k, v, sm_log2, w, none, s));
+  if (include_sink_window &&
+      failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v, sm_log2,
+                                     w, s),
+             "launch_partials"))
+    return ALSPEC_ERR_HIP;
+  return hip_status(
+      alspec::launch_partials(pa, p->kv_dtype, false, q, k, v, sm_log2, w, s),
+      "launch_partials");
 }
 
 alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
@@ -217,7 +292,8 @@ alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
   if ((st = check_ws(ws, ws_bytes, wl)) != ALSPEC_OK) return st;
   const alspec::WsPtrs w = alspec::ws_ptrs((void *)ws, wl);
   return hip_status(alspec::launch_lse_combine(pa, w, o_exact, lse_exact,
-                                               (hipStream_t)stream));
+                                               (hipStream_t)stream),
+                    "launch_lse_combine");
 }
 
 alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
@@ -232,7 +308,8 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
   if (st != ALSPEC_OK) return st;
   return hip_status(alspec::launch_verify(pa, o_approx, o_exact, ratio, commit,
                                           o_committed, p->lambda,
-                                          (hipStream_t)stream));
+                                          (hipStream_t)stream),
+                    "launch_verify");
 }
 
 alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
@@ -263,60 +340,137 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   const alspec_events &E = ev ? *ev : none;
   alspec::Outs o{o_approx, lse_approx, o_exact, lse_exact, ratio,
                  commit,   o_committed, p->lambda};
+  auto approx = [&](hipStream_t s) -> alspec_status {
+    alspec_status r = record(E.approx_begin, s);
+    if (r != ALSPEC_OK) return r;
+    if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
+                                       sm_log2, w, s),
+               "launch_partials") ||
+        failed(alspec::launch_approx_combine(pa, w, o, s),
+               "launch_approx_combine"))
+      return ALSPEC_ERR_HIP;
+    return record(E.approx_end, s);
+  };
+  auto middle = [&](hipStream_t s) -> alspec_status {
+    alspec_status r = record(E.exact_begin, s);
+    if (r != ALSPEC_OK) return r;
+    if (failed(alspec::launch_partials(pa, p->kv_dtype, false, q, k, v,
+                                       sm_log2, w, s),
+               "launch_partials"))
+      return ALSPEC_ERR_HIP;
+    return record(E.exact_end, s);
+  };
+  auto verify = [&](hipStream_t s) -> alspec_status {
+    if (failed(alspec::launch_merge_verify(pa, w, o, s),
+               "launch_merge_verify"))
+      return ALSPEC_ERR_HIP;
+    return record(E.verify_end, s);
+  };
 
-  if (!p->overlap) {
+  // Ordering after the last uncaptured fused call that used this
+  // workspace: its entry's event follows that call's verify, the last of
+  // its kernels to read the workspace.  Under stream capture the library
+  // adds no such ordering (the caller orders captured calls that share a
+  // workspace), and the pipelined mode, whose verify stream is the
+  // handle's, is refused.
+  const bool cap = capturing(se) || (two && capturing(sa));
+  if (p->overlap == 2 && cap) return ALSPEC_ERR_UNSUPPORTED;
+  bool fresh = false;
+  WsEntry *ent = cap ? nullptr : ws_entry(h, ws, &fresh);
+  auto wait_ws = [&](hipStream_t s) -> alspec_status {
+    if (!ent || !ent->used || ent->stream == s) return ALSPEC_OK;
+    return hip_status(hipStreamWaitEvent(s, ent->ev, 0), "hipStreamWaitEvent");
+  };
+  auto done_ws = [&](hipStream_t s) -> alspec_status {
+    if (!ent) return ALSPEC_OK;
+    if (failed(hipEventRecord(ent->ev, s), "hipEventRecord"))
+      return ALSPEC_ERR_HIP;
+    ent->ws = ws;
+    ent->stream = s;
+    ent->used = true;
+    ent->tick = ++h->tick;
+    return ALSPEC_OK;
+  };
+  // An evicted entry's workspace stays safe: the streams of this call are
+  // ordered after its last verify before the entry is reused.
+  if (fresh && (st = wait_ws(sa)) != ALSPEC_OK) return st;
+  if (fresh && two && (st = wait_ws(se)) != ALSPEC_OK) return st;
+  if (fresh) ent->used = false;
+
+  if (p->overlap == 0) {
     // Approximation first, then the exact pass, in one stream: no
     // cross-stream wait between the kernels.  The approximation stream is
     // handed o_approx through an event, so work queued there after this
     // call runs while the exact pass does.
-    if ((st = record(E.approx_begin, se)) != ALSPEC_OK) return st;
-    if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsApprox,
-                                true, q, k, v, sm_log2, w, o,
-                                se) != hipSuccess)
-      return ALSPEC_ERR_HIP;
-    if ((st = record(E.approx_end, se)) != ALSPEC_OK) return st;
+    if ((st = wait_ws(se)) != ALSPEC_OK) return st;
+    if ((st = approx(se)) != ALSPEC_OK) return st;
     if (two) {
-      if (hipEventRecord(h->ev_approx, se) != hipSuccess) return ALSPEC_ERR_HIP;
-      if (hipStreamWaitEvent(sa, h->ev_approx, 0) != hipSuccess)
+      if (failed(hipEventRecord(h->ev_approx, se), "hipEventRecord"))
+        return ALSPEC_ERR_HIP;
+      if (failed(hipStreamWaitEvent(sa, h->ev_approx, 0),
+                 "hipStreamWaitEvent"))
         return ALSPEC_ERR_HIP;
     }
-    if ((st = record(E.exact_begin, se)) != ALSPEC_OK) return st;
-    if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates,
-                                false, q, k, v, sm_log2, w, o,
-                                se) != hipSuccess)
+    if ((st = middle(se)) != ALSPEC_OK) return st;
+    if ((st = verify(se)) != ALSPEC_OK) return st;
+    return done_ws(se);
+  }
+
+  if (p->overlap == 2) {
+    // Pipelined: stream_exact carries only middle splits, so successive
+    // calls' exact passes run back to back; the approximation goes on
+    // stream_approx, and the merge, verify and commit on the handle's own
+    // verify stream once both are done.
+    if ((st = wait_ws(sa)) != ALSPEC_OK) return st;
+    if (two && (st = wait_ws(se)) != ALSPEC_OK) return st;
+    if ((st = approx(sa)) != ALSPEC_OK) return st;
+    if (failed(hipEventRecord(h->ev_approx, sa), "hipEventRecord"))
       return ALSPEC_ERR_HIP;
-    if ((st = record(E.exact_end, se)) != ALSPEC_OK) return st;
-    if (alspec::launch_merge_verify(pa, w, o, se) != hipSuccess)
+    if ((st = middle(se)) != ALSPEC_OK) return st;
+    if (failed(hipEventRecord(h->ev_mid, se), "hipEventRecord"))
       return ALSPEC_ERR_HIP;
-    return record(E.verify_end, se);
+    if (failed(hipStreamWaitEvent(h->sv, h->ev_approx, 0),
+               "hipStreamWaitEvent") ||
+        failed(hipStreamWaitEvent(h->sv, h->ev_mid, 0), "hipStreamWaitEvent"))
+      return ALSPEC_ERR_HIP;
+    if ((st = verify(h->sv)) != ALSPEC_OK) return st;
+    return done_ws(h->sv);
   }
 
   // Overlap: the approximation (on stream_approx) and the middle splits (on
-  // stream_exact) start together; the exact merge waits for both.  The
-  // approximation reuses this workspace, so it is first ordered after
-  // everything the exact stream already holds (earlier calls' merges).
-  if (two) {
-    if (hipEventRecord(h->ev_join, se) != hipSuccess) return ALSPEC_ERR_HIP;
-    if (hipStreamWaitEvent(sa, h->ev_join, 0) != hipSuccess)
+  // stream_exact) start together; the exact merge and verify follow on
+  // stream_exact once both are done.  Outside a capture the approximation,
+  // which rewrites this workspace, first waits for the last verify that
+  // read it, or with no record of one for everything already queued on
+  // stream_exact.
+  if (two && ent && ent->used) {
+    if ((st = wait_ws(sa)) != ALSPEC_OK) return st;
+    if ((st = wait_ws(se)) != ALSPEC_OK) return st;
+  } else if (two && ent) {
+    if (failed(hipEventRecord(h->ev_join, se), "hipEventRecord") ||
+        failed(hipStreamWaitEvent(sa, h->ev_join, 0), "hipStreamWaitEvent"))
       return ALSPEC_ERR_HIP;
+  } else if ((st = wait_ws(se)) != ALSPEC_OK) {
+    return st;
   }
-  if ((st = record(E.approx_begin, sa)) != ALSPEC_OK) return st;
-  if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsApprox, true,
-                              q, k, v, sm_log2, w, o, sa) != hipSuccess)
+  if ((st = approx(sa)) != ALSPEC_OK) return st;
+  if (two && failed(hipEventRecord(h->ev_approx, sa), "hipEventRecord"))
     return ALSPEC_ERR_HIP;
-  if ((st = record(E.approx_end, sa)) != ALSPEC_OK) return st;
-  if (two && hipEventRecord(h->ev_approx, sa) != hipSuccess)
+  if ((st = middle(se)) != ALSPEC_OK) return st;
+  if (two &&
+      failed(hipStreamWaitEvent(se, h->ev_approx, 0), "hipStreamWaitEvent"))
     return ALSPEC_ERR_HIP;
-  if ((st = record(E.exact_begin, se)) != ALSPEC_OK) return st;
-  if (alspec::launch_partials(pa, p->kv_dtype, alspec::kPartialsStates, false,
-                              q, k, v, sm_log2, w, o, se) != hipSuccess)
+  if ((st = verify(se)) != ALSPEC_OK) return st;
+  return done_ws(se);
+}
+
+alspec_status alspec_order_after_verify(alspec_handle *h, void *stream) {
+  if (!h) return ALSPEC_ERR_INVALID_ARG;
+  if (capturing((hipStream_t)stream)) return ALSPEC_ERR_UNSUPPORTED;
+  if (failed(hipEventRecord(h->ev_verify, h->sv), "hipEventRecord"))
     return ALSPEC_ERR_HIP;
-  if ((st = record(E.exact_end, se)) != ALSPEC_OK) return st;
-  if (two && hipStreamWaitEvent(se, h->ev_approx, 0) != hipSuccess)
-    return ALSPEC_ERR_HIP;
-  if (alspec::launch_merge_verify(pa, w, o, se) != hipSuccess)
-    return ALSPEC_ERR_HIP;
-  return record(E.verify_end, se);
+  return hip_status(hipStreamWaitEvent((hipStream_t)stream, h->ev_verify, 0),
+                    "hipStreamWaitEvent");
 }
 
 }  // extern "C"

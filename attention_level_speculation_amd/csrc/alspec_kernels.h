@@ -31,17 +31,16 @@ struct Outs {
   float lambda;
 };
 
-enum PartialsMode {
-  kPartialsStates = 0,  // split states only (sink+window or middle)
-  kPartialsApprox = 1   // sink+window states, merged into o_approx
-};
+// Split states over the sink and window splits (approx_set = true) or the
+// middle splits, into the workspace slots.
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
+                           const float *q, const void *k, const void *v,
+                           float sm_log2, const WsPtrs &w, hipStream_t s);
 
-// Split-state kernel over the sink and window splits (approx_set = true;
-// implied by kPartialsApprox) or the middle splits.
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, int mode,
-                           bool approx_set, const float *q, const void *k,
-                           const void *v, float sm_log2, const WsPtrs &w,
-                           const Outs &o, hipStream_t s);
+// Merge of the sink+window states (written by an earlier launch) into
+// o.o_approx, o.lse_approx and the reusable merged state.
+hipError_t launch_approx_combine(const PlanArgs &pa, const WsPtrs &w,
+                                 const Outs &o, hipStream_t s);
 
 // Exact merge of the stored sink+window state with the middle splits, then
 // the relative L2 verify, the commit flag and the committed output (o.*).

@@ -17,6 +17,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <tuple>
 #include <type_traits>
 
 #include "alspec_kernels.h"
@@ -313,7 +314,11 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 // Wave w takes tiles w, w + 4, ... of the range; the next tile's K and V
 // are loaded while the current one is computed.  Each wave keeps its own
 // online softmax; the waves are merged at the end.
-template <int G>
+// QLDS keeps the q operands in LDS (read per MFMA) instead of registers,
+// and PF prefetches the next tile; without both the footprint is small
+// enough for the sink/window kernel, the merges and the middle-split kernel
+// to share a CU (the middle-split kernel uses QLDS with PF).
+template <int G, bool QLDS, bool PF>
 __device__ void split_state_mfma(const float *__restrict__ qg,
                                  const uint16_t *__restrict__ kb,
                                  const uint16_t *__restrict__ vb, int t0,
@@ -366,8 +371,9 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
 
   // q of head r (columns r >= G are padding: a valid row is read and
   // zeroed, so the loads need no branch and go out together)
+  __shared__ bf16x8 s_q[QLDS ? 3 : 1][4][QLDS ? 64 : 1];
   bf16x8 qh[4], qm[4], ql[4];
-  {
+  if (!QLDS || wave == 0) {
     const float4 *qr =
         (const float4 *)(qg + (size_t)(r < G ? r : G - 1) * D + 32 * c);
     const float qs = r < G ? sm_log2 : 0.f;
@@ -381,22 +387,31 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
                           qv[2 * s + 1].x * qs, qv[2 * s + 1].y * qs,
                           qv[2 * s + 1].z * qs, qv[2 * s + 1].w * qs};
       split3(x, qh[s], qm[s], ql[s]);
+      if constexpr (QLDS) {
+        s_q[0][s][lane] = qh[s];
+        s_q[QLDS ? 1 : 0][s][lane] = qm[s];
+        s_q[QLDS ? 2 : 0][s][lane] = ql[s];
+      }
     }
   }
+  if constexpr (QLDS) __syncthreads();
 
   for (int blk = t0; blk < t1; blk += STEP) {
     const int tb = blk + wave * TILE;
     // next tile (rows at or past t1 are not read and come back as zero)
     u32x4 kn[4], vn[4];
-    load(tb + STEP, kn, vn);
+    if constexpr (PF) load(tb + STEP, kn, vn);
     // logits: lane holds tokens 4c + j of the tile for head r
     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[s]);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qh[s], a4, 0, 0, 0);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qm[s], a4, 0, 0, 0);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, ql[s], a4, 0, 0, 0);
+      const bf16x8 b0 = QLDS ? s_q[0][s][lane] : qh[s];
+      const bf16x8 b1 = QLDS ? s_q[QLDS ? 1 : 0][s][lane] : qm[s];
+      const bf16x8 b2 = QLDS ? s_q[QLDS ? 2 : 0][s][lane] : ql[s];
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b0, a4, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b1, a4, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b2, a4, 0, 0, 0);
     }
     float sv[4];
     float mx = neg_inf();
@@ -446,10 +461,14 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
         for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (!PF) {
+      load(tb + STEP, kr, vr);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kr[s] = kn[s];
-      vr[s] = vn[s];
+      for (int s = 0; s < 4; ++s) {
+        kr[s] = kn[s];
+        vr[s] = vn[s];
+      }
     }
   }
 
@@ -653,19 +672,22 @@ __device__ __forceinline__ float ratio_of(float num, float den) {
 // Returns true in every thread of the block for the last block to arrive at
 // `cnt` out of `total`; that block also resets the counter to zero.  The
 // block barrier orders all of this block's global writes before thread 0's
-// device-scope release fence and arrival; the last block's thread 0 then
-// fences again (acquire) before the barrier that lets its threads read
-// what the other blocks wrote.
+// device-scope release fence and arrival; only the last block's thread 0
+// then takes the device-scope acquire fence (which invalidates the L2 lines
+// other blocks may have written) before the barrier that lets its threads
+// read.  Keeping the acquire to one block per merge spares concurrently
+// streaming kernels from repeated cache invalidation.
 __device__ bool arrive_last(unsigned *cnt, unsigned total) {
   __shared__ int s_last;
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned old = atomicAdd(cnt, 1u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     const int last = (old == total - 1) ? 1 : 0;
     if (last) {
-      atomicExch(cnt, 0u);
-      __threadfence();
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     s_last = last;
   }
@@ -714,11 +736,11 @@ __device__ __forceinline__ Item decode_item(const PlanArgs &pa,
 
 // Slots merged per thread per memory round in the merges of the sink and
 // window states (a handful of splits).
-constexpr int kMergeRoundA = 16;
+constexpr int kMergeRoundA = 8;
 // ... and in the exact merges (many middle splits).
 constexpr int kMergeRoundM = 8;
 
-template <class KV, int D, int G>
+template <class KV, int D, int G, bool PF>
 __device__ __forceinline__ void split_any(const float *qg,
                                           const typename KV::elem *kb,
                                           const typename KV::elem *vb, int t0,
@@ -726,7 +748,8 @@ __device__ __forceinline__ void split_any(const float *qg,
                                           float2 *out_ml, float *out_acc) {
   if constexpr (std::is_same<KV, KvBf16>::value && D == 128 &&
                 (G == 4 || G == 8))
-    split_state_mfma<G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
+    split_state_mfma<G, true, PF>(qg, kb, vb, t0, t1, sm_log2, out_ml,
+                                  out_acc);
   else
     split_state<KV, D, G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
 }
@@ -854,50 +877,54 @@ __device__ void finalize_entry(const PlanArgs &pa, const WsPtrs &w, int b,
   }
 }
 
-constexpr int kStates = kPartialsStates;
-constexpr int kApprox = kPartialsApprox;
-
-// One block per work item.  With MODE == kApprox (sink and window items),
-// the last block of each (entry, kv head) -- counted with a workspace
-// counter -- also merges that head group's sink+window states into
-// o_approx / lse_approx and the reusable merged state.
-template <class KV, int D, int G, int MODE>
+// One block per work item (sink and window items when APPROX, else middle
+// items): the split state of the item's G query heads over its token range.
+// The long middle splits prefetch the next tile; the short sink and window
+// splits keep a footprint that fits beside a running middle pass.
+template <class KV, int D, int G, bool APPROX>
 __global__ __launch_bounds__(kThreads) void partials_kernel(
-    PlanArgs pa, bool approx_set, const float *__restrict__ q,
+    PlanArgs pa, const float *__restrict__ q,
     const typename KV::elem *__restrict__ k,
-    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w,
-    Outs o) {
-  const bool aset = MODE == kApprox || approx_set;
-  const Item it = decode_item(pa, aset, blockIdx.x);
+    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w) {
+  const Item it = decode_item(pa, APPROX, blockIdx.x);
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
-                      v + kv_off, it.t0, it.t1, sm_log2,
-                      w.part_ml + (size_t)it.slot * Hq + h0,
-                      w.part_acc + ((size_t)it.slot * Hq + h0) * D);
-  if constexpr (MODE == kApprox) {
-    const int nA = pa.nsink[it.b] + pa.nwin[it.b];
-    if (!arrive_last(w.counters + it.b * kMaxKvHeads + it.g, (unsigned)nA))
-      return;
-    __shared__ float r_acc[G * D];
-    __shared__ float r_m[G], r_l[G];
-    const size_t bh0 = (size_t)it.b * Hq + h0;
-    // no prior state; the stored-state slots only serve as valid addresses
-    merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc,
-                                    pa.slot_base[it.b], nA, Hq, h0, false,
-                                    w.stA_ml + bh0, w.stA_acc + bh0 * D,
-                                    r_acc, r_m, r_l);
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-      const int hh = idx / D;
-      w.stA_acc[bh0 * D + idx] = r_acc[idx];
-      o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
-    }
-    if (threadIdx.x < G) {
-      const int hh = threadIdx.x;
-      w.stA_ml[bh0 + hh] = make_float2(r_m[hh], r_l[hh]);
-      if (o.lse_approx) o.lse_approx[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
-    }
+  split_any<KV, D, G, !APPROX>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+                               v + kv_off, it.t0, it.t1, sm_log2,
+                               w.part_ml + (size_t)it.slot * Hq + h0,
+                               w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+}
+
+// Merge of one head group's sink and window states (one block per
+// (entry, kv head)) into o_approx / lse_approx and the reusable merged
+// state.  The split states come from an earlier kernel, so no fence is
+// needed, and the merge is the one the exact combine uses, so with an empty
+// middle both give the same bits.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void approx_combine_kernel(PlanArgs pa,
+                                                                  WsPtrs w,
+                                                                  Outs o) {
+  __shared__ float r_acc[G * D];
+  __shared__ float r_m[G], r_l[G];
+  const int Hq = pa.Hq;
+  const int b = blockIdx.x / pa.Hkv, g = blockIdx.x % pa.Hkv;
+  const int h0 = g * G;
+  const int nA = pa.nsink[b] + pa.nwin[b];
+  const size_t bh0 = (size_t)b * Hq + h0;
+  // no prior state; the stored-state slots only serve as valid addresses
+  merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc, pa.slot_base[b], nA,
+                                  Hq, h0, false, w.stA_ml + bh0,
+                                  w.stA_acc + bh0 * D, r_acc, r_m, r_l);
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D;
+    w.stA_acc[bh0 * D + idx] = r_acc[idx];
+    o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
+  }
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    w.stA_ml[bh0 + hh] = make_float2(r_m[hh], r_l[hh]);
+    if (o.lse_approx) o.lse_approx[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
   }
 }
 
@@ -974,51 +1001,64 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
 
 // ------------------------------------------------------------- dispatch ---
 
+// Launch whose status is that of this launch alone (hipLaunchKernel
+// returns it), not whatever error an earlier call in the thread left for
+// hipGetLastError.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block,
+                  hipStream_t s, Args... a) {
+  std::tuple<KArgs...> t(a...);
+  return std::apply(
+      [&](auto &...x) {
+        void *argv[] = {(void *)&x...};
+        return hipLaunchKernel((const void *)kern, grid, block, argv, 0, s);
+      },
+      t);
+}
+
 template <class KV, int D, int G>
-hipError_t partials_kg(const PlanArgs &pa, int mode, bool approx_set,
-                       const float *q, const void *k, const void *v,
-                       float sm_log2, const WsPtrs &w, const Outs &o,
-                       hipStream_t s) {
-  const bool aset = mode == kApprox || approx_set;
-  const int items = aset ? pa.itemA_pre[pa.B] : pa.itemM_pre[pa.B];
+hipError_t partials_kg(const PlanArgs &pa, bool approx_set, const float *q,
+                       const void *k, const void *v, float sm_log2,
+                       const WsPtrs &w, hipStream_t s) {
+  const int items = approx_set ? pa.itemA_pre[pa.B] : pa.itemM_pre[pa.B];
   if (items == 0) return hipSuccess;
   using E = typename KV::elem;
-  const E *kk = (const E *)k;
-  const E *vv = (const E *)v;
-  dim3 grid(items), block(kThreads);
-  switch (mode) {
-    case kStates:
-      hipLaunchKernelGGL((partials_kernel<KV, D, G, kStates>), grid, block, 0,
-                         s, pa, approx_set, q, kk, vv, sm_log2, w, o);
-      break;
-    case kApprox:
-      hipLaunchKernelGGL((partials_kernel<KV, D, G, kApprox>), grid, block, 0,
-                         s, pa, approx_set, q, kk, vv, sm_log2, w, o);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  auto kern = approx_set ? partials_kernel<KV, D, G, true>
+                         : partials_kernel<KV, D, G, false>;
+  return launch(kern, dim3(items), dim3(kThreads), s, pa, q, (const E *)k,
+                (const E *)v, sm_log2, w);
 }
 
 template <class KV, int D>
-hipError_t partials_g(const PlanArgs &pa, int mode, bool approx_set,
-                      const float *q, const void *k, const void *v,
-                      float sm_log2, const WsPtrs &w, const Outs &o,
-                      hipStream_t s) {
+hipError_t partials_g(const PlanArgs &pa, bool approx_set, const float *q,
+                      const void *k, const void *v, float sm_log2,
+                      const WsPtrs &w, hipStream_t s) {
   switch (pa.G) {
     case 1:
-      return partials_kg<KV, D, 1>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                   o, s);
+      return partials_kg<KV, D, 1>(pa, approx_set, q, k, v, sm_log2, w, s);
     case 2:
-      return partials_kg<KV, D, 2>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                   o, s);
+      return partials_kg<KV, D, 2>(pa, approx_set, q, k, v, sm_log2, w, s);
     case 4:
-      return partials_kg<KV, D, 4>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                   o, s);
+      return partials_kg<KV, D, 4>(pa, approx_set, q, k, v, sm_log2, w, s);
     case 8:
-      return partials_kg<KV, D, 8>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                   o, s);
+      return partials_kg<KV, D, 8>(pa, approx_set, q, k, v, sm_log2, w, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t approx_combine_d(const PlanArgs &pa, const WsPtrs &w,
+                            const Outs &o, hipStream_t s) {
+  dim3 grid(pa.B * pa.Hkv), block(kThreads);
+  switch (pa.G) {
+    case 1:
+      return launch(approx_combine_kernel<D, 1>, grid, block, s, pa, w, o);
+    case 2:
+      return launch(approx_combine_kernel<D, 2>, grid, block, s, pa, w, o);
+    case 4:
+      return launch(approx_combine_kernel<D, 4>, grid, block, s, pa, w, o);
+    case 8:
+      return launch(approx_combine_kernel<D, 8>, grid, block, s, pa, w, o);
   }
   return hipErrorInvalidValue;
 }
@@ -1029,25 +1069,19 @@ hipError_t lse_combine_d(const PlanArgs &pa, const WsPtrs &w, float *o_exact,
   dim3 grid(pa.B * pa.Hkv), block(kThreads);
   switch (pa.G) {
     case 1:
-      hipLaunchKernelGGL((lse_combine_kernel<D, 1>), grid, block, 0, s, pa, w,
-                         o_exact, lse_exact);
-      break;
+      return launch(lse_combine_kernel<D, 1>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
     case 2:
-      hipLaunchKernelGGL((lse_combine_kernel<D, 2>), grid, block, 0, s, pa, w,
-                         o_exact, lse_exact);
-      break;
+      return launch(lse_combine_kernel<D, 2>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
     case 4:
-      hipLaunchKernelGGL((lse_combine_kernel<D, 4>), grid, block, 0, s, pa, w,
-                         o_exact, lse_exact);
-      break;
+      return launch(lse_combine_kernel<D, 4>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
     case 8:
-      hipLaunchKernelGGL((lse_combine_kernel<D, 8>), grid, block, 0, s, pa, w,
-                         o_exact, lse_exact);
-      break;
-    default:
-      return hipErrorInvalidValue;
+      return launch(lse_combine_kernel<D, 8>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1064,32 +1098,31 @@ WsPtrs ws_ptrs(void *ws, const Workspace &wl) {
   return w;
 }
 
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, int mode,
-                           bool approx_set, const float *q, const void *k,
-                           const void *v, float sm_log2, const WsPtrs &w,
-                           const Outs &o, hipStream_t s) {
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
+                           const float *q, const void *k, const void *v,
+                           float sm_log2, const WsPtrs &w, hipStream_t s) {
   if (kv_dtype == ALSPEC_KV_BF16) {
     if (pa.D == 128)
-      return partials_g<KvBf16, 128>(pa, mode, approx_set, q, k, v, sm_log2,
-                                     w, o, s);
-    return partials_g<KvBf16, 64>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                  o, s);
+      return partials_g<KvBf16, 128>(pa, approx_set, q, k, v, sm_log2, w, s);
+    return partials_g<KvBf16, 64>(pa, approx_set, q, k, v, sm_log2, w, s);
   }
   if (pa.D == 128)
-    return partials_g<KvF32, 128>(pa, mode, approx_set, q, k, v, sm_log2, w,
-                                  o, s);
-  return partials_g<KvF32, 64>(pa, mode, approx_set, q, k, v, sm_log2, w, o,
-                               s);
+    return partials_g<KvF32, 128>(pa, approx_set, q, k, v, sm_log2, w, s);
+  return partials_g<KvF32, 64>(pa, approx_set, q, k, v, sm_log2, w, s);
+}
+
+hipError_t launch_approx_combine(const PlanArgs &pa, const WsPtrs &w,
+                                 const Outs &o, hipStream_t s) {
+  if (pa.D == 128) return approx_combine_d<128>(pa, w, o, s);
+  return approx_combine_d<64>(pa, w, o, s);
 }
 
 hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
                                const Outs &o, hipStream_t s) {
   dim3 grid(pa.B * pa.Hq), block(kThreads);
   if (pa.D == 128)
-    hipLaunchKernelGGL(merge_verify_kernel<128>, grid, block, 0, s, pa, w, o);
-  else
-    hipLaunchKernelGGL(merge_verify_kernel<64>, grid, block, 0, s, pa, w, o);
-  return hipGetLastError();
+    return launch(merge_verify_kernel<128>, grid, block, s, pa, w, o);
+  return launch(merge_verify_kernel<64>, grid, block, s, pa, w, o);
 }
 
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
@@ -1102,10 +1135,8 @@ hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,
                          const float *o_exact, float *ratio, uint8_t *commit,
                          float *o_committed, float lambda, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(pa.B), dim3(kThreads), 0, s,
-                     pa.Hq * pa.D, o_approx, o_exact, ratio, commit,
-                     o_committed, lambda);
-  return hipGetLastError();
+  return launch(verify_kernel, dim3(pa.B), dim3(kThreads), s, pa.Hq * pa.D,
+                o_approx, o_exact, ratio, commit, o_committed, lambda);
 }
 
 }  // namespace alspec

@@ -44,7 +44,7 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     return ALSPEC_ERR_INVALID_ARG;
   if (p->split_tokens < 0 || p->window_split_tokens < 0)
     return ALSPEC_ERR_INVALID_ARG;
-  if (p->overlap != 0 && p->overlap != 1) return ALSPEC_ERR_INVALID_ARG;
+  if (p->overlap < 0 || p->overlap > 2) return ALSPEC_ERR_INVALID_ARG;
   for (int b = 0; b < B && b < kMaxBatch; ++b)
     if (p->seq_lens[b] < 1 || p->seq_lens[b] > p->kv_capacity)
       return ALSPEC_ERR_INVALID_ARG;
@@ -88,10 +88,10 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     T = pow2_near(t);
   }
   // Window split length: the window is on the approximation's latency path,
-  // so it is cut into about 8 pieces that run side by side.
+  // so it is cut into about 16 pieces that run side by side.
   int Tw = p->window_split_tokens;
   if (Tw == 0) {
-    Tw = max_win / 8;
+    Tw = max_win / 16;
     if (Tw < 64) Tw = 64;
     if (Tw > 512) Tw = 512;
     Tw = pow2_floor(Tw);

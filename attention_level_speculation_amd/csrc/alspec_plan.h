@@ -15,11 +15,10 @@ constexpr int kMaxKvHeads = ALSPEC_MAX_KV_HEADS;
 constexpr size_t kWsAlign = 256;
 // counters at the start of every workspace, independent of the shape, so a
 // workspace reused for another shape still finds them at zero:
-//   [0, kUserCounters)                 sink+window merge, per (b, g)
 //   [kUserCounters, + kMaxBatch)       heads done (exact merge), per b
-constexpr int kUserCounters = kMaxBatch * kMaxKvHeads;
+constexpr int kUserCounters = 0;
 constexpr int kNumCounters = kUserCounters + kMaxBatch;
-constexpr size_t kCounterBytes = 65536;
+constexpr size_t kCounterBytes = 4096;
 static_assert(kNumCounters * 4 <= (int)kCounterBytes, "counter region");
 
 // Everything a kernel needs to map a block index to its work; passed by

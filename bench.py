@@ -7,22 +7,37 @@ Workload (the headline long-context case): one user's decode token through
 head dim 128, bf16 KV with fp32 arithmetic, context 131072 (512 MiB of KV
 per layer), sink 4, window 2048, lambda 0.10 -- for needle densities
 0, 1, 2, 4, 8 and 16 per kv head.  All 6 x 32 layers (96 GiB) are drawn on
-the device by the seeded generator and stay resident; a step is one token
-through the 32 layers of one density (densities rotate step by step), each
-layer one fused call of the library (approximation on one stream, exact
-split-K pass, merge and verify on another).
+the device by the seeded generator and stay resident.  A step is one token
+through the 32 layers of one density (densities rotate step by step); each
+layer is one fused call of the library: sink+window approximation, exact
+split-K pass over the middle, merge, relative-L2 verify and commit.
 
-Reported: tokens*layers/s (whole-job throughput, inputs resident in HBM),
-KV GB/s of the exact split-K kernel against the HBM peak (HIP events
-around every launch, on the stream it runs on), the speculation hit rate per
-density, the approximation's and the exact path's latency per layer and the
-critical-path time a commit saves, the HBM probe, and the CPU oracle timed
-on a bounded sample of the same layers.
+Schedules (overlap modes of the library):
+  pipelined  -- the speculative order, captured once per density as a HIP
+                graph and replayed (overlap mode 1): each layer's
+                approximation on one stream; its exact split-K pass on a
+                second stream after the previous layer's approximation
+                (under speculation the query comes from it), then the
+                merge, verify and commit there; every layer has its own
+                workspace, so no approximation waits for an earlier verify.
+  sequential -- every layer's approximation, exact pass and verify one
+                after another on one stream (overlap mode 0), captured as
+                a HIP graph likewise.
+  pipelined_eager_verify_stream -- overlap mode 2, issued eagerly (it runs
+                merge/verify on the handle's own stream, which is not
+                captured): context for the host-bound eager case.
+The headline value is the pipelined throughput.
+
+Also reported: KV GB/s of the exact split-K kernel against the HBM peak
+(HIP events around every launch of it in eagerly issued steps of the same
+schedules, on the stream it runs on), the speculation
+hit rate per density, each layer's time to its approximate and to its
+verified output and the critical-path time a commit saves, the HBM probe,
+and the CPU oracle timed on a bounded sample of the same layers.
 """
 import argparse
 import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -34,6 +49,8 @@ if ROOT not in sys.path:
 METRIC = ("spec flash-decode tokens·layers/s + KV GB/s (% HBM peak) at "
           "128K; hit rate")
 HBM_PEAK_GBPS = 8000.0
+EVENT_NAMES = ("approx_begin", "approx_end", "exact_begin", "exact_end",
+               "verify_end")
 
 
 def parse_args():
@@ -45,13 +62,13 @@ def parse_args():
     ap.add_argument("--densities", default="0,1,2,4,8,16")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--window-split-tokens", type=int, default=0)
-    ap.add_argument("--overlap", type=int, default=0,
-                    help="1: start the exact pass together with the "
-                         "approximation instead of after it")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="run approximation and exact pass on one stream")
+    ap.add_argument("--ws-ring", type=int, default=2,
+                    help="workspaces the eager pipelined schedule cycles "
+                         "through")
+    ap.add_argument("--schedules", default="pipe,seq,pipe_vs",
+                    help="schedules to time (pipe is the headline)")
     ap.add_argument("--no-events", action="store_true",
-                    help="time without per-launch events (no roofline)")
+                    help="skip the instrumented runs (no roofline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
@@ -81,6 +98,7 @@ def main():
     from synth import gen
 
     dens = [int(x) for x in args.densities.split(",")]
+    nd = len(dens)
     nl = args.layers
     works = [gen.llama8b_128k(needles=n) for n in dens]
     w0 = works[0]
@@ -105,10 +123,14 @@ def main():
         log(f"drew needles={dens[di]}: {nl} layers "
             f"({2 * K.numel() * 2 / 2**30:.1f} GiB) t={time.time() - t0:.1f}s")
 
-    p = al.params_for(w0, split_tokens=args.split_tokens,
-                      window_split_tokens=args.window_split_tokens,
-                      overlap=args.overlap)
-    splits, (T, Tw) = al.plan_splits(p, 0)
+    def params(overlap):
+        return al.params_for(w0, split_tokens=args.split_tokens,
+                             window_split_tokens=args.window_split_tokens,
+                             overlap=overlap)
+    # schedules: name -> (overlap mode, captured as a graph)
+    modes = {"pipe": (1, True), "seq": (0, True), "pipe_vs": (2, False)}
+    P = {m: params(ov) for m, (ov, _) in modes.items()}
+    splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
     mid_tokens = sum(e - b for k, b, e in splits if k == 2)
     a_tokens = sum(e - b for k, b, e in splits if k != 2)
@@ -116,13 +138,22 @@ def main():
     mid_bytes = mid_tokens * bytes_per_token * w0.B   # one exact launch
     layer_bytes = sum(w0.seq_lens) * bytes_per_token  # every KV byte
     h = al.Handle(0)
-    ws = al.alloc_workspace(p, dev)
-    outs = [[al.alloc_outputs(p, dev) for _ in range(nl)] for _ in dens]
+    # workspaces: the sequential schedule runs each call on one stream and
+    # reuses one; each captured pipelined layer gets its own (the library
+    # adds no workspace ordering under capture); the eager pipelined
+    # schedule cycles through a ring, ordered by the library
+    n_ws = {"seq": 1, "pipe": nl, "pipe_vs": args.ws_ring}
+    WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
+          for m in modes}
+    outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
+            for _ in range(nd)]
     sa = torch.cuda.Stream(device=dev)
-    se = sa if args.one_stream else torch.cuda.Stream(device=dev)
+    se = torch.cuda.Stream(device=dev)
+    cap = torch.cuda.Stream(device=dev)
+    cur = torch.cuda.current_stream()
+    fn = B_._spec_decode
 
-    # pre-marshalled C-ABI arguments of every (density, layer) call
-    def call_args(di, layer):
+    def call_args(p, di, layer, ws):
         o = outs[di][layer]
         return [h.ptr, ctypes.byref(p), Qs[di][layer].data_ptr(),
                 Ks[di][layer].data_ptr(), Vs[di][layer].data_ptr(),
@@ -131,86 +162,138 @@ def main():
                 o["ratio"].data_ptr(), o["commit"].data_ptr(),
                 o["o_committed"].data_ptr(), ws.data_ptr(), ws.numel(),
                 sa.cuda_stream, se.cuda_stream]
-    ARGS = [[call_args(di, layer) for layer in range(nl)]
-            for di in range(len(dens))]
-    fn = B_._spec_decode
+    A = {m: [[call_args(P[m], di, l, WS[m][l % len(WS[m])])
+              for l in range(nl)] for di in range(nd)] for m in modes}
 
-    def run_step(step, evsets=None):
-        di = step % len(dens)
+    def new_events():
+        evs = {n: torch.cuda.Event(enable_timing=True) for n in EVENT_NAMES}
+        for ev_ in evs.values():
+            ev_.record(se)           # torch creates the hipEvent on record
+        return B_.Events(*[evs[n].cuda_event for n in EVENT_NAMES]), evs
+
+    def enqueue(mode, di, evrow=None):
+        """One step (all layers of density di) on sa/se; evrow: per-layer
+        (Events struct, dict) for instrumented runs."""
         for layer in range(nl):
-            ev = None
-            if evsets is not None:
-                ev = ctypes.byref(evsets[step][layer][0])
-            st = fn(*ARGS[di][layer], ev)
+            if mode != "seq" and layer > 0:
+                # layer l's exact pass needs its query, which under
+                # speculation comes from layer l-1's approximation: the
+                # approximation stream holds nothing after it
+                se.wait_stream(sa)
+            ev = None if evrow is None else ctypes.byref(evrow[layer][0])
+            st = fn(*A[mode][di][layer], ev)
             if st != 0:
                 raise al.AlspecError(st, "alspec_spec_decode")
 
-    # ---- warmup and timed region --------------------------------------
-    torch.cuda.synchronize()
-    for s in range(args.warmup):
-        run_step(s)
-    torch.cuda.synchronize()
-    evsets = None
-    if not args.no_events:
-        names = ("approx_begin", "approx_end", "exact_begin", "exact_end",
-                 "verify_end")
-        evsets = []
-        for s in range(args.steps):
-            row = []
-            for layer in range(nl):
-                evs = {n: torch.cuda.Event(enable_timing=True) for n in names}
-                for ev_ in evs.values():
-                    ev_.record(se)   # torch creates the hipEvent lazily
-                st = B_.Events(*[evs[n].cuda_event for n in names])
-                row.append((st, evs))
-            evsets.append(row)
-    log(f"timed region: {args.steps} steps x {nl} layers, split {T} "
-        f"(middle splits {n_mid}), window split {Tw}")
-    torch.cuda.synchronize()          # barrier: one rank
-    ref_ev = torch.cuda.Event(enable_timing=True)
-    ref_ev.record(se)
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        run_step(s, evsets)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    wall = t_end - t_start
-    ms_per_step = wall / args.steps * 1e3
-    tok_layers_per_s = w0.B * nl * args.steps / wall
+    def issue(mode, di, evrow=None):
+        """One eager step, ordered after the current stream and joined
+        back into it."""
+        sa.wait_stream(cur)
+        se.wait_stream(cur)
+        enqueue(mode, di, evrow)
+        if modes[mode][0] == 2:
+            al.order_after_verify(h, cur)
+        cur.wait_stream(sa)
+        cur.wait_stream(se)
 
-    # ---- per-launch timings -------------------------------------------
-    # every event is read against one reference event recorded before the
-    # timed region, so times on the two streams share one origin
-    res = {}
-    if evsets is not None:
-        def at(ev):
-            return ref_ev.elapsed_time(ev) * 1e3   # microseconds
-        ex, t_ap, t_ex, saved, tot = [], [], [], 0.0, 0.0
+    def capture(mode, di):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            sa.wait_stream(cap)
+            se.wait_stream(cap)
+            enqueue(mode, di)
+            cap.wait_stream(sa)
+            cap.wait_stream(se)
+        return g
+
+    torch.cuda.synchronize()
+    if "pipe" not in args.schedules.split(","):
+        sys.exit("the pipelined schedule (pipe) is the headline; keep it")
+    graphs = {m: [capture(m, di) for di in range(nd)]
+              for m, (_, g) in modes.items()
+              if g and m in args.schedules.split(",")}
+    log(f"plan: split {T} (middle splits {n_mid}), window split {Tw}; "
+        f"captured {len(graphs) * nd} step graphs")
+
+    def timed(mode):
+        def step(s_):
+            if mode in graphs:
+                graphs[mode][s_ % nd].replay()
+            else:
+                issue(mode, s_ % nd)
+        torch.cuda.synchronize()
+        for s_ in range(args.warmup):
+            step(s_)
+        torch.cuda.synchronize()          # barrier: one rank
+        t_start = time.perf_counter()
         for s_ in range(args.steps):
-            di = s_ % len(dens)
-            for layer in range(nl):
-                e = evsets[s_][layer][1]
-                a0, a1 = at(e["approx_begin"]), at(e["approx_end"])
-                e0, e1 = at(e["exact_begin"]), at(e["exact_end"])
-                v1 = at(e["verify_end"])
-                start = min(a0, e0)
-                ex.append(e1 - e0)
-                t_ap.append(a1 - start)
-                t_ex.append(v1 - start)
-                if int(outs[di][layer]["commit"][0].item()):
-                    saved += max(0.0, v1 - a1)
-                tot += v1 - start
-        ex = np.array(ex)
-        res = {
-            "exact_kernel_us_mean": float(ex.mean()),
-            "exact_kernel_us_p10": float(np.percentile(ex, 10)),
-            "exact_kernel_us_p90": float(np.percentile(ex, 90)),
-            "approx_ready_us_mean": float(np.mean(t_ap)),
-            "exact_ready_us_mean": float(np.mean(t_ex)),
-            "critical_path_saved_frac": saved / tot if tot > 0 else 0.0,
-        }
-        res["approx_over_exact"] = (res["approx_ready_us_mean"] /
-                                    res["exact_ready_us_mean"])
+            step(s_)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_start
+
+    res = {}
+    sched = args.schedules.split(",")
+    for mode, key in (("pipe", "pipelined"), ("seq", "sequential"),
+                      ("pipe_vs", "pipelined_eager_verify_stream")):
+        if mode not in sched:
+            continue
+        wall_ = timed(mode)
+        log(f"{key}: {args.steps} steps in {wall_:.3f} s")
+        res[key] = {"overlap_mode": modes[mode][0],
+                    "hip_graph": modes[mode][1],
+                    "ms_per_step": wall_ / args.steps * 1e3,
+                    "tokens_layers_per_s": w0.B * nl * args.steps / wall_}
+    wall_pipe = res["pipelined"]["ms_per_step"] * args.steps / 1e3
+
+    # ---- instrumented runs: HIP events around every kernel --------------
+    # (eager calls: the HIP runtime loaded with torch rejects event records
+    # inside a stream capture, so the events bracket eagerly issued steps
+    # of the same schedule, each recorded on the stream its kernel runs on)
+    if not args.no_events:
+        for mode, key in (("pipe", "pipelined"), ("seq", "sequential")):
+            if mode not in sched:
+                continue
+            rows = [[new_events() for _ in range(nl)] for _ in range(nd)]
+            ex, t_ap, t_ex, saved, tot = [], [], [], 0.0, 0.0
+            reps = max(1, args.steps // nd)
+            for rep in range(reps + 1):
+                for di in range(nd):
+                    torch.cuda.synchronize()
+                    ref_ev = torch.cuda.Event(enable_timing=True)
+                    ref_ev.record(cur)
+                    issue(mode, di, rows[di])
+                    torch.cuda.synchronize()
+                    if rep == 0:
+                        continue          # warm-up pass
+
+                    def at(ev):
+                        return ref_ev.elapsed_time(ev) * 1e3   # us
+                    for layer in range(nl):
+                        e = rows[di][layer][1]
+                        a0, a1 = at(e["approx_begin"]), at(e["approx_end"])
+                        e0, e1 = at(e["exact_begin"]), at(e["exact_end"])
+                        v1 = at(e["verify_end"])
+                        ex.append(e1 - e0)
+                        # a pipelined layer starts when its exact pass can:
+                        # after the previous layer's approximation
+                        start = a0 if mode == "seq" else e0
+                        t_ap.append(a1 - start)
+                        t_ex.append(v1 - start)
+                        if int(outs[di][layer]["commit"][0].item()):
+                            saved += max(0.0, v1 - a1)
+                        tot += v1 - start
+            ex = np.array(ex)
+            res[key].update({
+                "exact_kernel_us_mean": float(ex.mean()),
+                "exact_kernel_us_p10": float(np.percentile(ex, 10)),
+                "exact_kernel_us_p90": float(np.percentile(ex, 90)),
+                "exact_kernel_launches_timed": int(ex.size),
+                "approx_ready_us_mean": float(np.mean(t_ap)),
+                "exact_ready_us_mean": float(np.mean(t_ex)),
+                "approx_over_exact": float(np.mean(t_ap) / np.mean(t_ex)),
+                "critical_path_saved_frac": saved / tot if tot > 0 else 0.0,
+            })
+        log("instrumented runs done")
 
     # ---- hit rate -------------------------------------------------------
     hits = {}
@@ -221,14 +304,15 @@ def main():
         allc += c
     hit_rate = sum(allc) / len(allc)
 
+    wall = wall_pipe
     out = {
         "metric": METRIC,
-        "value": tok_layers_per_s,
+        "value": w0.B * nl * args.steps / wall,
         "unit": "tokens·layers/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -240,13 +324,13 @@ def main():
                         "batch 1, 32 q / 8 kv heads, head dim 128, bf16 KV, "
                         f"{nl} layers, sink 4, window 2048, lambda 0.10, "
                         f"needles per kv head {dens}",
+            "schedule": "pipelined (speculative order, overlap mode 1), one "
+                        "HIP graph per step",
             "kv_dtype": "bf16", "arith": "f32", "context": w0.L_cap,
             "batch": w0.B, "layers": nl, "num_q_heads": w0.Hq,
             "num_kv_heads": w0.Hkv, "head_dim": w0.D, "sink": w0.S,
             "window": w0.W, "lambda": w0.lam, "split_tokens": T,
             "window_split_tokens": Tw, "middle_splits_per_head": n_mid,
-            "streams": 1 if args.one_stream else 2,
-            "overlap": args.overlap,
             "generator": {"a": w0.const.a, "c_s": w0.const.c_s,
                           "tau_s": w0.const.tau_s, "c_n": w0.const.c_n,
                           "tau_n": w0.const.tau_n},
@@ -258,14 +342,16 @@ def main():
     }
     out["step_hbm_frac"] = out["step_kv_GBps"] / HBM_PEAK_GBPS
     out.update(res)
-    if res:
-        achieved = mid_bytes / (res["exact_kernel_us_mean"] * 1e-6) / 1e9
+    if "exact_kernel_us_mean" in res["pipelined"]:
+        us = res["pipelined"]["exact_kernel_us_mean"]
+        achieved = mid_bytes / (us * 1e-6) / 1e9
         out["roofline"] = {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None,
-            "kernel": "partials_kernel<KvBf16,128,4> (middle splits)",
+            "kernel": "partials_kernel<KvBf16,128,4,false> (middle splits)",
             "algorithmic_bytes_per_launch": mid_bytes,
+            "launch_us_mean": us,
             "approx_tokens_per_head": a_tokens,
         }
 
@@ -274,10 +360,13 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, works, dens, outs, nl, Qs,
                                            Ks, Vs)
 
-    # ---- HBM probe ----------------------------------------------------------
+    # ---- HBM probe ------------------------------------------------------
     if not args.no_probe:
-        del Ks, Vs
-        ARGS = None
+        del graphs
+        Ks.clear()
+        Vs.clear()
+        A.clear()
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
         pr = sdev.probe_bandwidth()
         out["probe"] = {k: round(v["GBps"], 1) for k, v in pr.items()}

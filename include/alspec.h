@@ -62,7 +62,8 @@ extern "C" {
 typedef enum {
   ALSPEC_OK = 0,
   ALSPEC_ERR_INVALID_ARG = 1, /* null pointer, bad size, out-of-range value */
-  ALSPEC_ERR_UNSUPPORTED = 2, /* valid but outside the built shapes */
+  ALSPEC_ERR_UNSUPPORTED = 2, /* valid, but outside the built shapes or
+                                 not available in this context */
   ALSPEC_ERR_WORKSPACE = 3,   /* workspace too small or misaligned */
   ALSPEC_ERR_HIP = 4          /* the HIP runtime reported an error */
 } alspec_status;
@@ -84,9 +85,8 @@ typedef struct {
   float lambda;         /* verify threshold, >= 0 (+inf allowed, NaN not) */
   int32_t split_tokens;        /* middle split length; 0 = automatic */
   int32_t window_split_tokens; /* window split length; 0 = automatic */
-  int32_t overlap; /* fused call only: 0 = the exact pass starts once the
-                      approximation is done (it then has the GPU to itself
-                      and is ready soonest); 1 = both start together */
+  int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
+                      2 = pipelined (see alspec_spec_decode) */
 } alspec_params;
 
 #define ALSPEC_MAX_BATCH 64
@@ -94,9 +94,15 @@ typedef struct {
 /* group sizes G = Hq / Hkv that are built: 1, 2, 4, 8 */
 
 /* Optional timing events recorded around the fused call's kernels (any
- * member may be NULL).  approx_* are recorded on the approximation stream,
- * the others on the exact stream; exact_begin/exact_end bracket only the
- * middle split-K kernel. */
+ * member may be NULL; each a hipEvent_t created with timing enabled).
+ * approx_* bracket the approximation's kernels, exact_begin/exact_end only
+ * the middle split-K kernel, verify_end follows the merge and verify.  They
+ * are recorded on the stream that runs those kernels: in overlap mode 0
+ * all on stream_exact; in mode 1 approx_* on stream_approx; in mode 2 also
+ * verify_end on the handle's verify stream.  Inside a stream capture they
+ * are recorded with hipEventRecordExternal (timestamp nodes of the graph);
+ * a HIP runtime without that support fails the call with ALSPEC_ERR_HIP,
+ * so pass NULL events to calls that are captured. */
 typedef struct {
   void *approx_begin, *approx_end;
   void *exact_begin, *exact_end;
@@ -110,6 +116,12 @@ const char *alspec_status_string(alspec_status s);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t alspec_version(void);
+
+/* Text naming the HIP call and HIP error behind the most recent
+ * ALSPEC_ERR_HIP returned on the calling thread ("" if none yet).  The
+ * string is thread-local and stays valid until the thread's next failing
+ * call. */
+const char *alspec_last_error(void);
 
 /* Bytes of workspace the compute calls need for these parameters.  Pure
  * host computation (no GPU needed); validates the parameters. */
@@ -196,14 +208,41 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
  * splits, then the merge with the reused sink/window state, the verify and
  * the commit.  stream_approx is made to wait for the approximation only,
  * so work enqueued on stream_approx after this call may consume o_approx
- * while the exact pass runs.  With p->overlap == 1 the approximation runs
- * on stream_approx while the middle splits start on stream_exact; the
- * exact merge and verify then wait for both (stream_approx is first
- * ordered after the work already queued on stream_exact, so successive
- * calls on one workspace are safe).  Results are identical in both modes.
- * The two streams may be the same stream.  `ev` may be NULL.  Buffers
- * written by a call must not be read by the caller's own work until it is
- * ordered after the call's completion on the stream named above.
+ * while the exact pass runs.
+ *
+ * With p->overlap == 1 the approximation runs on stream_approx while the
+ * middle splits run on stream_exact; the exact merge, verify and commit
+ * follow on stream_exact once both are done.  Successive calls (under
+ * speculation, the layers of one decode step, each exact pass ordered by
+ * the caller after the approximation that produced its q) pipeline when
+ * each approximation needs to wait only for an earlier verify on its own
+ * workspace.  This mode may be captured into a HIP graph.
+ *
+ * With p->overlap == 2 (pipelined, uncaptured calls only) stream_exact
+ * carries only the middle splits, so successive calls' exact passes run
+ * back to back; the approximation runs on stream_approx (o_approx,
+ * lse_approx complete in its order), and the merge, verify and commit run
+ * on a stream owned by the handle once both are done, overlapping the next
+ * call's exact pass; alspec_order_after_verify orders a caller's stream
+ * after them.  Under stream capture this mode returns
+ * ALSPEC_ERR_UNSUPPORTED before enqueueing anything.
+ *
+ * Workspace ordering: for uncaptured calls the handle remembers, for the
+ * 16 most recently used workspaces, the event after the last fused call's
+ * verify on it, and orders a later fused call on that workspace after it
+ * (an overlap-1 call on a workspace with no such record first orders
+ * stream_approx after all work queued on stream_exact).  Under stream
+ * capture the library adds no workspace ordering: captured calls that
+ * share a workspace, graph launches and uncaptured calls that share one,
+ * and the standalone calls are ordered by the caller (for a captured
+ * overlap-1 pipeline, simplest by giving each call its own workspace).
+ * Ordering the exact pass after whatever produced q is the caller's task,
+ * as for any input.
+ *
+ * Results are identical in all modes.  The two streams may be the same
+ * stream.  `ev` may be NULL.  Buffers written by a call must not be read by
+ * the caller's own work until it is ordered after the call's completion on
+ * the stream named above.
  */
 alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  const float *q, const void *k, const void *v,
@@ -213,6 +252,11 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  float *o_committed, void *ws,
                                  size_t ws_bytes, void *stream_approx,
                                  void *stream_exact, const alspec_events *ev);
+
+/* Orders `stream` after all merge, verify and commit work that pipelined
+ * calls (p->overlap == 2) on this handle have enqueued so far.  Not for
+ * use under stream capture. */
+alspec_status alspec_order_after_verify(alspec_handle *h, void *stream);
 
 #ifdef __cplusplus
 }

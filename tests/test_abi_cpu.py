@@ -59,7 +59,7 @@ def P(**kw):
     (dict(sink=0, window=0), 1), (dict(sink=-1), 1), (dict(window=-5), 1),
     (dict(lam=-0.5), 1), (dict(lam=float("nan")), 1),
     (dict(sm_scale=0.0), 1), (dict(sm_scale=float("inf")), 1),
-    (dict(kv_dtype=7), 1), (dict(split_tokens=-1), 1), (dict(overlap=2), 1),
+    (dict(kv_dtype=7), 1), (dict(split_tokens=-1), 1), (dict(overlap=3), 1),
     (dict(head_dim=96), 2), (dict(num_q_heads=48, num_kv_heads=2), 2),
     (dict(batch=65, kv_capacity=10), 2), (dict(num_kv_heads=128,
                                               num_q_heads=128), 2),
@@ -139,11 +139,11 @@ def test_split_plan_tiles_context(seed):
 
 def test_headline_plan_shape():
     """Context 131072, S 4, W 2048, 8 kv heads: one sink split, window cut
-    into 8 pieces of 256, middle pieces of 2048 (about two items per CU)."""
+    into 16 pieces of 128, middle pieces of 2048 (about two items per CU)."""
     p = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1)
     splits, (T, Tw) = al.plan_splits(p, 0)
-    assert Tw == 256 and T == 2048
-    assert sum(1 for s in splits if s[0] == 1) == 8
+    assert Tw == 128 and T == 2048
+    assert sum(1 for s in splits if s[0] == 1) == 16
     assert sum(1 for s in splits if s[0] == 2) == 63
     _check_tiling(p, 0, 131072, 4, 2048)
 
@@ -152,3 +152,7 @@ def test_workspace_grows_with_splits():
     a = al.workspace_size(P(split_tokens=1024))
     b = al.workspace_size(P(split_tokens=64))
     assert b > a
+
+
+def test_last_error_is_a_string():
+    assert isinstance(al.last_error(), str)
