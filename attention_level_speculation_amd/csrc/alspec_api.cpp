@@ -371,10 +371,9 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   // workspace: its entry's event follows that call's verify, the last of
   // its kernels to read the workspace.  Under stream capture the library
   // adds no such ordering (the caller orders captured calls that share a
-  // workspace), and the pipelined mode, whose verify stream is the
-  // handle's, is refused.
+  // workspace): there such a wait could make a stream wait on a branch of
+  // the capture that was forked from that same stream.
   const bool cap = capturing(se) || (two && capturing(sa));
-  if (p->overlap == 2 && cap) return ALSPEC_ERR_UNSUPPORTED;
   bool fresh = false;
   WsEntry *ent = cap ? nullptr : ws_entry(h, ws, &fresh);
   auto wait_ws = [&](hipStream_t s) -> alspec_status {
@@ -466,7 +465,20 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
 
 alspec_status alspec_order_after_verify(alspec_handle *h, void *stream) {
   if (!h) return ALSPEC_ERR_INVALID_ARG;
-  if (capturing((hipStream_t)stream)) return ALSPEC_ERR_UNSUPPORTED;
+  // The verify stream is part of a capture only after a pipelined call was
+  // captured; it must then belong to the caller's capture, and it holds
+  // nothing to order a capturing stream after otherwise.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone, vs = cs;
+  unsigned long long cid = 0, vid = 0;
+  if (failed(hipStreamGetCaptureInfo((hipStream_t)stream, &cs, &cid),
+             "hipStreamGetCaptureInfo") ||
+      failed(hipStreamGetCaptureInfo(h->sv, &vs, &vid),
+             "hipStreamGetCaptureInfo"))
+    return ALSPEC_ERR_HIP;
+  const bool c_on = cs == hipStreamCaptureStatusActive;
+  const bool v_on = vs == hipStreamCaptureStatusActive;
+  if (v_on && (!c_on || cid != vid)) return ALSPEC_ERR_UNSUPPORTED;
+  if (c_on && !v_on) return ALSPEC_OK;
   if (failed(hipEventRecord(h->ev_verify, h->sv), "hipEventRecord"))
     return ALSPEC_ERR_HIP;
   return hip_status(hipStreamWaitEvent((hipStream_t)stream, h->ev_verify, 0),

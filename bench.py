@@ -13,24 +13,27 @@ layer is one fused call of the library: sink+window approximation, exact
 split-K pass over the middle, merge, relative-L2 verify and commit.
 
 Schedules (overlap modes of the library):
-  pipelined  -- the speculative order, captured once per density as a HIP
-                graph and replayed (overlap mode 1): each layer's
-                approximation on one stream; its exact split-K pass on a
-                second stream after the previous layer's approximation
-                (under speculation the query comes from it), then the
-                merge, verify and commit there; every layer has its own
-                workspace, so no approximation waits for an earlier verify.
+  pipelined  -- the speculative order (overlap mode 2), captured once per
+                density as a HIP graph and replayed: the exact split-K
+                passes of successive layers back to back on one stream,
+                each after the previous layer's approximation (under
+                speculation the query comes from it); approximations on a
+                second stream; merge, verify and commit on the library's
+                verify stream, off the exact passes' path.  Every layer has
+                its own workspace.
+  pipelined_verify_on_exact_stream -- the same with overlap mode 1 (merge
+                and verify between successive exact passes), as a graph.
   sequential -- every layer's approximation, exact pass and verify one
-                after another on one stream (overlap mode 0), captured as
-                a HIP graph likewise.
-  pipelined_eager_verify_stream -- overlap mode 2, issued eagerly (it runs
-                merge/verify on the handle's own stream, which is not
-                captured): context for the host-bound eager case.
-The headline value is the pipelined throughput.
+                after another on one stream (overlap mode 0), as a graph.
+  pipelined_eager -- overlap mode 2 issued call by call without a graph
+                (host-bound: context only).
+The headline value is the throughput of the fastest of them (named in
+config.schedule); all compute the same outputs.
 
 Also reported: KV GB/s of the exact split-K kernel against the HBM peak
-(HIP events around every launch of it in eagerly issued steps of the same
-schedules, on the stream it runs on), the speculation
+(HIP events on its stream around back-to-back launches of it over all
+resident layers), per-kernel HIP events in eagerly issued steps of the
+schedules, the speculation
 hit rate per density, each layer's time to its approximate and to its
 verified output and the critical-path time a commit saves, the HBM probe,
 and the CPU oracle timed on a bounded sample of the same layers.
@@ -52,6 +55,30 @@ HBM_PEAK_GBPS = 8000.0
 EVENT_NAMES = ("approx_begin", "approx_end", "exact_begin", "exact_end",
                "verify_end")
 
+# HBM bytes per launch of the exact split-K kernel on this workload, from
+# rocprofv3 FETCH_SIZE and WRITE_SIZE runs, scaled by what the counters read
+# for a copy kernel of known size (fetch x2.000, write x1.000).  Valid only
+# for the kernel sources they were taken on (sha256 of the files below);
+# once those change the figure is withheld until measured again.
+TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip",
+                       "attention_level_speculation_amd/csrc/alspec_kernels.h",
+                       "attention_level_speculation_amd/csrc/alspec_plan.h"),
+           "sha256": "a620f42f89a6be8c965f72af913e8f24"
+                     "d6428c005410f4d7f55a451a1d72c8c2",
+           "fetch_bytes": 258200.8 * 1024 * 2.0,
+           "write_bytes": 1023.8 * 1024 * 1.0}
+
+
+def measured_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != TRAFFIC["sha256"]:
+        return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -62,13 +89,16 @@ def parse_args():
     ap.add_argument("--densities", default="0,1,2,4,8,16")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--window-split-tokens", type=int, default=0)
-    ap.add_argument("--ws-ring", type=int, default=2,
+    ap.add_argument("--ws-ring", type=int, default=0,
                     help="workspaces the eager pipelined schedule cycles "
-                         "through")
-    ap.add_argument("--schedules", default="pipe,seq,pipe_vs",
+                         "through (0: one per layer)")
+    ap.add_argument("--schedules", default="pipe,pipe1,seq,pipe_eager",
                     help="schedules to time (pipe is the headline)")
     ap.add_argument("--no-events", action="store_true",
-                    help="skip the instrumented runs (no roofline)")
+                    help="skip the instrumented runs (per-layer latencies)")
+    ap.add_argument("--kernel-launches", type=int, default=768,
+                    help="back-to-back launches of the exact split-K kernel "
+                         "timed for the roofline (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
@@ -128,7 +158,8 @@ def main():
                              window_split_tokens=args.window_split_tokens,
                              overlap=overlap)
     # schedules: name -> (overlap mode, captured as a graph)
-    modes = {"pipe": (1, True), "seq": (0, True), "pipe_vs": (2, False)}
+    modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
+             "pipe_eager": (2, False)}
     P = {m: params(ov) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
@@ -142,7 +173,8 @@ def main():
     # reuses one; each captured pipelined layer gets its own (the library
     # adds no workspace ordering under capture); the eager pipelined
     # schedule cycles through a ring, ordered by the library
-    n_ws = {"seq": 1, "pipe": nl, "pipe_vs": args.ws_ring}
+    n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
+            "pipe_eager": args.ws_ring or nl}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
     outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
@@ -202,6 +234,8 @@ def main():
             sa.wait_stream(cap)
             se.wait_stream(cap)
             enqueue(mode, di)
+            if modes[mode][0] == 2:
+                al.order_after_verify(h, cap)   # joins the verify stream
             cap.wait_stream(sa)
             cap.wait_stream(se)
         return g
@@ -233,8 +267,10 @@ def main():
 
     res = {}
     sched = args.schedules.split(",")
-    for mode, key in (("pipe", "pipelined"), ("seq", "sequential"),
-                      ("pipe_vs", "pipelined_eager_verify_stream")):
+    for mode, key in (("pipe", "pipelined"),
+                      ("pipe1", "pipelined_verify_on_exact_stream"),
+                      ("seq", "sequential"),
+                      ("pipe_eager", "pipelined_eager")):
         if mode not in sched:
             continue
         wall_ = timed(mode)
@@ -243,7 +279,9 @@ def main():
                     "hip_graph": modes[mode][1],
                     "ms_per_step": wall_ / args.steps * 1e3,
                     "tokens_layers_per_s": w0.B * nl * args.steps / wall_}
-    wall_pipe = res["pipelined"]["ms_per_step"] * args.steps / 1e3
+    # headline: the fastest schedule (each computes the same outputs)
+    best = max(res, key=lambda k_: res[k_]["tokens_layers_per_s"])
+    wall = res[best]["ms_per_step"] * args.steps / 1e3
 
     # ---- instrumented runs: HIP events around every kernel --------------
     # (eager calls: the HIP runtime loaded with torch rejects event records
@@ -274,24 +312,24 @@ def main():
                         e0, e1 = at(e["exact_begin"]), at(e["exact_end"])
                         v1 = at(e["verify_end"])
                         ex.append(e1 - e0)
-                        # a pipelined layer starts when its exact pass can:
-                        # after the previous layer's approximation
-                        start = a0 if mode == "seq" else e0
-                        t_ap.append(a1 - start)
-                        t_ex.append(v1 - start)
+                        # approximate output: its kernels' span; verified
+                        # output: from the exact pass's start
+                        t_ap.append(a1 - a0)
+                        t_ex.append(v1 - e0)
                         if int(outs[di][layer]["commit"][0].item()):
                             saved += max(0.0, v1 - a1)
-                        tot += v1 - start
+                        tot += max(v1, a1) - min(a0, e0)
             ex = np.array(ex)
             res[key].update({
                 "exact_kernel_us_mean": float(ex.mean()),
                 "exact_kernel_us_p10": float(np.percentile(ex, 10)),
                 "exact_kernel_us_p90": float(np.percentile(ex, 90)),
                 "exact_kernel_launches_timed": int(ex.size),
-                "approx_ready_us_mean": float(np.mean(t_ap)),
-                "exact_ready_us_mean": float(np.mean(t_ex)),
+                "approx_latency_us_mean": float(np.mean(t_ap)),
+                "exact_latency_us_mean": float(np.mean(t_ex)),
                 "approx_over_exact": float(np.mean(t_ap) / np.mean(t_ex)),
-                "critical_path_saved_frac": saved / tot if tot > 0 else 0.0,
+                "committed_time_saved_frac": saved / tot if tot > 0 else 0.0,
+                "instrumented_schedule": "eager, HIP events per kernel",
             })
         log("instrumented runs done")
 
@@ -304,7 +342,6 @@ def main():
         allc += c
     hit_rate = sum(allc) / len(allc)
 
-    wall = wall_pipe
     out = {
         "metric": METRIC,
         "value": w0.B * nl * args.steps / wall,
@@ -324,8 +361,7 @@ def main():
                         "batch 1, 32 q / 8 kv heads, head dim 128, bf16 KV, "
                         f"{nl} layers, sink 4, window 2048, lambda 0.10, "
                         f"needles per kv head {dens}",
-            "schedule": "pipelined (speculative order, overlap mode 1), one "
-                        "HIP graph per step",
+            "schedule": best,
             "kv_dtype": "bf16", "arith": "f32", "context": w0.L_cap,
             "batch": w0.B, "layers": nl, "num_q_heads": w0.Hq,
             "num_kv_heads": w0.Hkv, "head_dim": w0.D, "sink": w0.S,
@@ -342,16 +378,18 @@ def main():
     }
     out["step_hbm_frac"] = out["step_kv_GBps"] / HBM_PEAK_GBPS
     out.update(res)
-    if "exact_kernel_us_mean" in res["pipelined"]:
-        us = res["pipelined"]["exact_kernel_us_mean"]
+    if args.kernel_launches > 0:
+        us = kernel_timing(args, al, B_, h, P["seq"], Qs, Ks, Vs, se, nd, nl)
         achieved = mid_bytes / (us * 1e-6) / 1e9
         out["roofline"] = {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
-            "kernel": "partials_kernel<KvBf16,128,4,false> (middle splits)",
+            "traffic": measured_traffic(),
+            "kernel": "partials_kernel<KvBf16,128,4,false> (exact split-K "
+                      "pass over the middle)",
             "algorithmic_bytes_per_launch": mid_bytes,
             "launch_us_mean": us,
+            "launches_timed": args.kernel_launches,
             "approx_tokens_per_head": a_tokens,
         }
 
@@ -376,6 +414,36 @@ def main():
 
     print(json.dumps(out), flush=True)
     h.close()
+
+
+def kernel_timing(args, al, B_, h, p, Qs, Ks, Vs, stream, nd, nl):
+    """Average duration of the exact split-K kernel: back-to-back launches
+    (alspec_flash_decode_exact over the middle splits) over every resident
+    layer in turn, bracketed by two HIP events on the stream they run on;
+    elapsed time / launches (so inter-launch gaps count against it)."""
+    import torch
+    ws = al.alloc_workspace(p)
+    order = [(di, layer) for layer in range(nl) for di in range(nd)]
+    args_ = [(h.ptr, ctypes.byref(p), Qs[di][layer].data_ptr(),
+              Ks[di][layer].data_ptr(), Vs[di][layer].data_ptr(), 0,
+              ws.data_ptr(), ws.numel(), stream.cuda_stream)
+             for di, layer in order]
+    fn = B_._flash_exact
+
+    def run(n):
+        for i in range(n):
+            st = fn(*args_[i % len(args_)])
+            if st != 0:
+                raise al.AlspecError(st, "alspec_flash_decode_exact")
+    torch.cuda.synchronize()
+    run(16)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(args.kernel_launches)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / args.kernel_launches
 
 
 def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
@@ -406,7 +474,17 @@ def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
                      abs(r["ratio"][0] - w.lam) <= 1e-4)
         if secs >= args.cpu_seconds:
             break
+    # the same oracle on one core, one layer
+    di, layer = order[0]
+    w = works[di]
+    q = Qs[di][layer].cpu().numpy()
+    k = Ks[di][layer].view(torch.int16).cpu().numpy().view(np.uint16)
+    v = Vs[di][layer].view(torch.int16).cpu().numpy().view(np.uint16)
+    t = time.perf_counter()
+    oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam, threads=1)
+    one = time.perf_counter() - t
     return {"value": n * works[0].B / secs, "unit": "tokens·layers/s",
+            "one_core_value": works[0].B / one,
             "cores": threads, "kind": "oracle",
             "sample": f"{n} of the {len(dens) * nl} (needles, layer) pairs "
                       "of the same workload: whole layers (32 heads, context "

@@ -218,14 +218,15 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
  * each approximation needs to wait only for an earlier verify on its own
  * workspace.  This mode may be captured into a HIP graph.
  *
- * With p->overlap == 2 (pipelined, uncaptured calls only) stream_exact
+ * With p->overlap == 2 (pipelined) stream_exact
  * carries only the middle splits, so successive calls' exact passes run
  * back to back; the approximation runs on stream_approx (o_approx,
  * lse_approx complete in its order), and the merge, verify and commit run
  * on a stream owned by the handle once both are done, overlapping the next
  * call's exact pass; alspec_order_after_verify orders a caller's stream
- * after them.  Under stream capture this mode returns
- * ALSPEC_ERR_UNSUPPORTED before enqueueing anything.
+ * after them.  Under stream capture the verify stream joins the capture;
+ * the capture must then call alspec_order_after_verify on a capturing
+ * stream before it ends, which joins it back.
  *
  * Workspace ordering: for uncaptured calls the handle remembers, for the
  * 16 most recently used workspaces, the event after the last fused call's
@@ -254,8 +255,11 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  void *stream_exact, const alspec_events *ev);
 
 /* Orders `stream` after all merge, verify and commit work that pipelined
- * calls (p->overlap == 2) on this handle have enqueued so far.  Not for
- * use under stream capture. */
+ * calls (p->overlap == 2) on this handle have enqueued so far.  Under
+ * stream capture: joins the handle's verify stream back into the capture
+ * of `stream` (OK and no work if no pipelined call was captured);
+ * ALSPEC_ERR_UNSUPPORTED if the verify stream is part of another capture
+ * or `stream` is not capturing while it is. */
 alspec_status alspec_order_after_verify(alspec_handle *h, void *stream);
 
 #ifdef __cplusplus
