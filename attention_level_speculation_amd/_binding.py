@@ -10,7 +10,9 @@ import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libalspec.so")
+# ALSPEC_LIB selects another build of the same library (e.g. a variant
+# built with different compile-time options); default: the in-tree build.
+LIB_PATH = os.environ.get("ALSPEC_LIB") or os.path.join(HERE, "libalspec.so")
 
 KV_F32 = 0
 KV_BF16 = 1

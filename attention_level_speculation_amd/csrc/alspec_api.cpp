@@ -196,8 +196,13 @@ alspec_status alspec_create(int device, alspec_handle **out) {
     st = ALSPEC_ERR_INVALID_ARG;
   } else {
     h->device = device;
+    // The handle's events only order work between streams of this device,
+    // so they skip the system-scope cache writeback and invalidation a
+    // default event performs when it completes (which stalls, and slows,
+    // the streaming kernels around it).
     auto event = [](hipEvent_t *e) {
-      return !failed(hipEventCreateWithFlags(e, hipEventDisableTiming),
+      return !failed(hipEventCreateWithFlags(
+                         e, hipEventDisableTiming | hipEventDisableSystemFence),
                      "hipEventCreateWithFlags");
     };
     bool ok = event(&h->ev_join) && event(&h->ev_approx) &&

@@ -27,6 +27,12 @@ namespace alspec {
 namespace {
 
 constexpr int kThreads = 256;
+// Tiles of K/V in flight beyond the one being computed, in the middle-split
+// loop: 1 (two register sets) or 2 (three).
+#ifndef ALSPEC_PREFETCH_DEPTH
+#define ALSPEC_PREFETCH_DEPTH 1
+#endif
+constexpr int kPrefetchDepth = ALSPEC_PREFETCH_DEPTH;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -348,26 +354,27 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
 
+  // Rows past the range are clamped to its last row (a row of this same
+  // range, so no address outside it is formed); their logits are masked to
+  // -inf below, so they carry no weight.  Unconditional loads keep the
+  // memory pipeline free of branches.
+  const int last = t1 - 1;
   auto load = [&](int tb, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
-    const int krow = tb + r;
+    const int krow = min(tb + r, last);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kk[s] = u32x4{0u, 0u, 0u, 0u};
-      if (krow < t1)
-        kk[s] = *(const u32x4 *)(kb + (size_t)krow * D + 32 * c + 8 * s);
-    }
+    for (int s = 0; s < 4; ++s)
+      kk[s] = *(const u32x4 *)(kb + (size_t)krow * D + 32 * c + 8 * s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int vrow = tb + 4 * c + j;
-      vv[j] = u32x4{0u, 0u, 0u, 0u};
-      if (vrow < t1) vv[j] = *(const u32x4 *)(vb + (size_t)vrow * D + 8 * r);
+      const int vrow = min(tb + 4 * c + j, last);
+      vv[j] = *(const u32x4 *)(vb + (size_t)vrow * D + 8 * r);
     }
   };
 
   // The first tile's loads go out before q is read and split, so the two
   // round trips overlap.
-  u32x4 kr[4], vr[4];
-  load(t0 + wave * TILE, kr, vr);
+  u32x4 ka[4], va[4], kb2[4], vb2[4];
+  if (t0 < t1) load(t0 + wave * TILE, ka, va);
 
   // q of head r (columns r >= G are padding: a valid row is read and
   // zeroed, so the loads need no branch and go out together)
@@ -396,11 +403,8 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
   }
   if constexpr (QLDS) __syncthreads();
 
-  for (int blk = t0; blk < t1; blk += STEP) {
-    const int tb = blk + wave * TILE;
-    // next tile (rows at or past t1 are not read and come back as zero)
-    u32x4 kn[4], vn[4];
-    if constexpr (PF) load(tb + STEP, kn, vn);
+  // One 16-token tile of this wave: logits on MFMA, online softmax, P*V.
+  auto tile = [&](int tb, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
     // logits: lane holds tokens 4c + j of the tile for head r
     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -461,14 +465,42 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
         for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
     }
     __builtin_amdgcn_wave_barrier();
-    if constexpr (!PF) {
-      load(tb + STEP, kr, vr);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        kr[s] = kn[s];
-        vr[s] = vn[s];
-      }
+  };
+
+  if constexpr (PF && kPrefetchDepth >= 2) {
+    // Three register sets in turn: two tiles' loads are in flight while the
+    // current one is computed; no set is copied into another, so a wait
+    // covers only the loads of the tile about to be used.
+    u32x4 kc[4], vc[4];
+    if (t0 + STEP < t1) load(t0 + STEP + wave * TILE, kb2, vb2);
+    for (int blk = t0; blk < t1; blk += 3 * STEP) {
+      const int ta = blk + wave * TILE;
+      load(ta + 2 * STEP, kc, vc);
+      tile(ta, ka, va);
+      if (blk + STEP >= t1) break;
+      load(ta + 3 * STEP, ka, va);
+      tile(ta + STEP, kb2, vb2);
+      if (blk + 2 * STEP >= t1) break;
+      load(ta + 4 * STEP, kb2, vb2);
+      tile(ta + 2 * STEP, kc, vc);
+    }
+  } else if constexpr (PF) {
+    // Two register sets in turn: the next tile's loads are in flight while
+    // the current one is computed, and no set is copied into the other, so
+    // a wait covers only the loads of the tile about to be used.
+    for (int blk = t0; blk < t1; blk += 2 * STEP) {
+      const int ta = blk + wave * TILE;
+      load(ta + STEP, kb2, vb2);
+      tile(ta, ka, va);
+      if (blk + STEP >= t1) break;
+      load(ta + 2 * STEP, ka, va);
+      tile(ta + STEP, kb2, vb2);
+    }
+  } else {
+    for (int blk = t0; blk < t1; blk += STEP) {
+      const int ta = blk + wave * TILE;
+      if (blk != t0) load(ta, ka, va);
+      tile(ta, ka, va);
     }
   }
 

@@ -203,15 +203,35 @@ def main():
             ev_.record(se)           # torch creates the hipEvent on record
         return B_.Events(*[evs[n].cuda_event for n in EVENT_NAMES]), evs
 
+    # Chain events: layer l's exact pass needs its query, which under
+    # speculation comes from layer l-1's approximation.  They only order
+    # two streams of this device, so they are created without the
+    # system-scope fence a default event takes on completion (the HIP
+    # runtime torch loaded, reached by its soname).
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_uint]
+    chain = []
+    for _ in range(nl):
+        e_ = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e_),
+                                       0x2 | 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        chain.append(e_)
+    sa_p, se_p = ctypes.c_void_p(sa.cuda_stream), ctypes.c_void_p(se.cuda_stream)
+
     def enqueue(mode, di, evrow=None):
         """One step (all layers of density di) on sa/se; evrow: per-layer
         (Events struct, dict) for instrumented runs."""
         for layer in range(nl):
             if mode != "seq" and layer > 0:
-                # layer l's exact pass needs its query, which under
-                # speculation comes from layer l-1's approximation: the
-                # approximation stream holds nothing after it
-                se.wait_stream(sa)
+                # the approximation stream holds nothing after the previous
+                # layer's approximation
+                if (hip.hipEventRecord(chain[layer], sa_p) != 0 or
+                        hip.hipStreamWaitEvent(se_p, chain[layer], 0) != 0):
+                    raise RuntimeError("chain event failed")
             ev = None if evrow is None else ctypes.byref(evrow[layer][0])
             st = fn(*A[mode][di][layer], ev)
             if st != 0:
