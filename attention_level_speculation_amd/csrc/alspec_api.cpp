@@ -249,12 +249,11 @@ alspec_status alspec_sink_approx(alspec_handle *h, const alspec_params *p,
   alspec::Outs o{};
   o.o_approx = o_approx;
   o.lse_approx = lse_approx;
-  hipStream_t s = (hipStream_t)stream;
-  if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
-                              p->sm_scale * kLog2e, w, s), "launch_partials"))
-    return ALSPEC_ERR_HIP;
-  return hip_status(alspec::launch_approx_combine(pa, w, o, s),
-                    "launch_approx_combine");
+  return hip_status(
+      alspec::launch_approx_fused(pa, p->kv_dtype, q, k, v,
+                                  p->sm_scale * kLog2e, w, o,
+                                  (hipStream_t)stream),
+      "launch_approx_fused");
 }
 
 alspec_status alspec_flash_decode_exact(alspec_handle *h,
@@ -345,15 +344,23 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   const alspec_events &E = ev ? *ev : none;
   alspec::Outs o{o_approx, lse_approx, o_exact, lse_exact, ratio,
                  commit,   o_committed, p->lambda};
+  // The sequential schedule runs the approximation in one launch; where it
+  // runs beside the streaming middle pass it takes two fence-free launches.
   auto approx = [&](hipStream_t s) -> alspec_status {
     alspec_status r = record(E.approx_begin, s);
     if (r != ALSPEC_OK) return r;
-    if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
-                                       sm_log2, w, s),
-               "launch_partials") ||
-        failed(alspec::launch_approx_combine(pa, w, o, s),
-               "launch_approx_combine"))
+    if (p->overlap == 0) {
+      if (failed(alspec::launch_approx_fused(pa, p->kv_dtype, q, k, v,
+                                             sm_log2, w, o, s),
+                 "launch_approx_fused"))
+        return ALSPEC_ERR_HIP;
+    } else if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
+                                              sm_log2, w, s),
+                      "launch_partials") ||
+               failed(alspec::launch_approx_combine(pa, w, o, s),
+                      "launch_approx_combine")) {
       return ALSPEC_ERR_HIP;
+    }
     return record(E.approx_end, s);
   };
   auto middle = [&](hipStream_t s) -> alspec_status {

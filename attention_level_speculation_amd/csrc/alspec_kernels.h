@@ -37,6 +37,14 @@ hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
                            const float *q, const void *k, const void *v,
                            float sm_log2, const WsPtrs &w, hipStream_t s);
 
+// The whole approximation in one launch (split states, then the merge by
+// the last block of each (entry, kv head)): o.o_approx, o.lse_approx and the
+// reusable merged state.
+hipError_t launch_approx_fused(const PlanArgs &pa, int kv_dtype,
+                               const float *q, const void *k, const void *v,
+                               float sm_log2, const WsPtrs &w, const Outs &o,
+                               hipStream_t s);
+
 // Merge of the sink+window states (written by an earlier launch) into
 // o.o_approx, o.lse_approx and the reusable merged state.
 hipError_t launch_approx_combine(const PlanArgs &pa, const WsPtrs &w,

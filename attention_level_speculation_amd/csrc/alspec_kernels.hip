@@ -922,25 +922,21 @@ __global__ __launch_bounds__(kThreads) void partials_kernel(
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G, !APPROX>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
-                               v + kv_off, it.t0, it.t1, sm_log2,
-                               w.part_ml + (size_t)it.slot * Hq + h0,
-                               w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+                            v + kv_off, it.t0, it.t1, sm_log2,
+                            w.part_ml + (size_t)it.slot * Hq + h0,
+                            w.part_acc + ((size_t)it.slot * Hq + h0) * D);
 }
 
-// Merge of one head group's sink and window states (one block per
-// (entry, kv head)) into o_approx / lse_approx and the reusable merged
-// state.  The split states come from an earlier kernel, so no fence is
-// needed, and the merge is the one the exact combine uses, so with an empty
-// middle both give the same bits.
+// Merge of the sink and window states of entry b, kv head g into o_approx /
+// lse_approx and the reusable merged state.  The exact combine uses the
+// same merge, so with an empty middle both give the same bits.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void approx_combine_kernel(PlanArgs pa,
-                                                                  WsPtrs w,
-                                                                  Outs o) {
+__device__ void approx_merge(const PlanArgs &pa, const WsPtrs &w,
+                             const Outs &o, int b, int g) {
   __shared__ float r_acc[G * D];
   __shared__ float r_m[G], r_l[G];
   const int Hq = pa.Hq;
-  const int b = blockIdx.x / pa.Hkv, g = blockIdx.x % pa.Hkv;
   const int h0 = g * G;
   const int nA = pa.nsink[b] + pa.nwin[b];
   const size_t bh0 = (size_t)b * Hq + h0;
@@ -958,6 +954,42 @@ __global__ __launch_bounds__(kThreads) void approx_combine_kernel(PlanArgs pa,
     w.stA_ml[bh0 + hh] = make_float2(r_m[hh], r_l[hh]);
     if (o.lse_approx) o.lse_approx[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
   }
+}
+
+// The whole approximation in one launch: each block computes one sink or
+// window split, and the last block of an (entry, kv head) to finish merges
+// the group's states.  Saves the second launch on the approximation's
+// latency path; its fences (a device-scope release per block, an acquire
+// in the last one) are why the schedules whose approximation runs beside
+// the streaming middle pass use the two-launch form instead.
+template <class KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void approx_fused_kernel(
+    PlanArgs pa, const float *__restrict__ q,
+    const typename KV::elem *__restrict__ k,
+    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w,
+    Outs o) {
+  const Item it = decode_item(pa, true, blockIdx.x);
+  const int Hq = pa.Hq;
+  const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
+  const int h0 = it.g * G;
+  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+                            v + kv_off, it.t0, it.t1, sm_log2,
+                            w.part_ml + (size_t)it.slot * Hq + h0,
+                            w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+  const unsigned n = (unsigned)(pa.nsink[it.b] + pa.nwin[it.b]);
+  if (!arrive_last(w.counters + kApproxCounters + it.b * pa.Hkv + it.g, n))
+    return;
+  approx_merge<D, G>(pa, w, o, it.b, it.g);
+}
+
+// Merge of one head group's sink and window states (one block per
+// (entry, kv head)).  The split states come from an earlier kernel, so no
+// fence is needed.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void approx_combine_kernel(PlanArgs pa,
+                                                                  WsPtrs w,
+                                                                  Outs o) {
+  approx_merge<D, G>(pa, w, o, blockIdx.x / pa.Hkv, blockIdx.x % pa.Hkv);
 }
 
 // Exact merge, verify and commit: one block per (entry, query head) merges
@@ -1078,6 +1110,34 @@ hipError_t partials_g(const PlanArgs &pa, bool approx_set, const float *q,
   return hipErrorInvalidValue;
 }
 
+template <class KV, int D, int G>
+hipError_t approx_fused_kg(const PlanArgs &pa, const float *q, const void *k,
+                           const void *v, float sm_log2, const WsPtrs &w,
+                           const Outs &o, hipStream_t s) {
+  const int items = pa.itemA_pre[pa.B];
+  if (items == 0) return hipSuccess;
+  using E = typename KV::elem;
+  return launch(approx_fused_kernel<KV, D, G>, dim3(items), dim3(kThreads), s,
+                pa, q, (const E *)k, (const E *)v, sm_log2, w, o);
+}
+
+template <class KV, int D>
+hipError_t approx_fused_g(const PlanArgs &pa, const float *q, const void *k,
+                          const void *v, float sm_log2, const WsPtrs &w,
+                          const Outs &o, hipStream_t s) {
+  switch (pa.G) {
+    case 1:
+      return approx_fused_kg<KV, D, 1>(pa, q, k, v, sm_log2, w, o, s);
+    case 2:
+      return approx_fused_kg<KV, D, 2>(pa, q, k, v, sm_log2, w, o, s);
+    case 4:
+      return approx_fused_kg<KV, D, 4>(pa, q, k, v, sm_log2, w, o, s);
+    case 8:
+      return approx_fused_kg<KV, D, 8>(pa, q, k, v, sm_log2, w, o, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D>
 hipError_t approx_combine_d(const PlanArgs &pa, const WsPtrs &w,
                             const Outs &o, hipStream_t s) {
@@ -1141,6 +1201,20 @@ hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
   if (pa.D == 128)
     return partials_g<KvF32, 128>(pa, approx_set, q, k, v, sm_log2, w, s);
   return partials_g<KvF32, 64>(pa, approx_set, q, k, v, sm_log2, w, s);
+}
+
+hipError_t launch_approx_fused(const PlanArgs &pa, int kv_dtype,
+                               const float *q, const void *k, const void *v,
+                               float sm_log2, const WsPtrs &w, const Outs &o,
+                               hipStream_t s) {
+  if (kv_dtype == ALSPEC_KV_BF16) {
+    if (pa.D == 128)
+      return approx_fused_g<KvBf16, 128>(pa, q, k, v, sm_log2, w, o, s);
+    return approx_fused_g<KvBf16, 64>(pa, q, k, v, sm_log2, w, o, s);
+  }
+  if (pa.D == 128)
+    return approx_fused_g<KvF32, 128>(pa, q, k, v, sm_log2, w, o, s);
+  return approx_fused_g<KvF32, 64>(pa, q, k, v, sm_log2, w, o, s);
 }
 
 hipError_t launch_approx_combine(const PlanArgs &pa, const WsPtrs &w,

@@ -15,11 +15,14 @@ constexpr int kMaxKvHeads = ALSPEC_MAX_KV_HEADS;
 constexpr size_t kWsAlign = 256;
 // counters at the start of every workspace, independent of the shape, so a
 // workspace reused for another shape still finds them at zero:
-//   [kUserCounters, + kMaxBatch)       heads done (exact merge), per b
+//   [kUserCounters, + kMaxBatch)        heads done (exact merge), per b
+//   [kApproxCounters, + kMaxBatch * kMaxKvHeads)
+//                                       sink/window splits done (one-launch
+//                                       approximation), per (b, kv head)
 constexpr int kUserCounters = 0;
-constexpr int kNumCounters = kUserCounters + kMaxBatch;
-constexpr size_t kCounterBytes = 4096;
-static_assert(kNumCounters * 4 <= (int)kCounterBytes, "counter region");
+constexpr int kApproxCounters = kUserCounters + kMaxBatch;
+constexpr int kNumCounters = kApproxCounters + kMaxBatch * kMaxKvHeads;
+constexpr size_t kCounterBytes = (kNumCounters * 4 + 255) / 256 * 256;
 
 // Everything a kernel needs to map a block index to its work; passed by
 // value as a kernel argument.
