@@ -100,6 +100,15 @@ def test_multiuser_ragged_full_size(handle):
         compare(got, ref, "bf16", lam, f"multiuser lam={lam}")
         print(f"[case] commits {got['commit'].tolist()} oracle "
               f"{ref['commit'].tolist()}", flush=True)
+    # the one-launch approximation (sequential mode) and the two-launch one
+    # (overlapped modes) give the same bits with 8 users x 8 kv heads
+    seq = run_fused(al, handle, al.params_for(w), qd, kd, vd)
+    for ov in (1, 2):
+        other = run_fused(al, handle, al.params_for(w, overlap=ov), qd, kd, vd)
+        for key in seq:
+            assert np.array_equal(seq[key], other[key]), (ov, key)
+    alone = run_standalone(al, handle, al.params_for(w), qd, kd, vd)
+    assert np.array_equal(alone["o_approx"], seq["o_approx"])
 
 
 def test_llama70b_full_size(handle):
