@@ -63,9 +63,9 @@ EVENT_NAMES = ("approx_begin", "approx_end", "exact_begin", "exact_end",
 TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip",
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h"),
-           "sha256": "a620f42f89a6be8c965f72af913e8f24"
-                     "d6428c005410f4d7f55a451a1d72c8c2",
-           "fetch_bytes": 258200.8 * 1024 * 2.0,
+           "sha256": "78dd6c6993024be1264d4ffcf7c1cc35"
+                     "4bd984d8ae106739bff9daaf21a53fa8",
+           "fetch_bytes": 258222.3 * 1024 * 2.0,
            "write_bytes": 1023.8 * 1024 * 1.0}
 
 
