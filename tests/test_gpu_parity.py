@@ -123,6 +123,8 @@ def _mk(name, B, Hq, Hkv, D, lens, dt, S, W, lam=0.1, needles=1, seed=7):
                         needles=[needles] * B, seed=seed)
 
 
+MAX_B_LENS = [1, 2, 4, 5, 131, 132, 133] + [137 + 37 * i for i in range(57)]
+
 EDGE = [
     # name, B, Hq, Hkv, D, lens, dtype, S, W, split, wsplit
     ("g1_d64_f32", 2, 4, 4, 64, [777, 1500], "f32", 4, 100, 0, 0),
@@ -137,6 +139,11 @@ EDGE = [
     ("short_inside_sink", 3, 8, 2, 64, [1, 2, 3], "f32", 4, 0, 0, 0),
     ("cover_exact", 2, 8, 2, 128, [132, 100], "bf16", 4, 128, 0, 0),
     ("window_only_long", 1, 8, 8, 128, [4096], "bf16", 0, 1, 0, 0),
+    # maximum batch (64 users, ragged down to a single token, around the
+    # sink + window boundary) and maximum kv heads
+    ("max_batch_f32", 64, 8, 8, 64, MAX_B_LENS, "f32", 4, 128, 0, 0),
+    ("max_batch_g4_bf16", 64, 32, 8, 128, MAX_B_LENS, "bf16", 4, 128, 0, 0),
+    ("max_kv_heads", 1, 64, 64, 128, [1700], "bf16", 4, 128, 0, 0),
 ]
 
 
