@@ -31,6 +31,16 @@ static bool capturing(hipStream_t s) {
          status == hipStreamCaptureStatusActive;
 }
 
+// Id of the capture `s` belongs to (0: not capturing).
+static unsigned long long capture_id(hipStream_t s) {
+  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  if (hipStreamGetCaptureInfo(s, &status, &id) != hipSuccess ||
+      status != hipStreamCaptureStatusActive)
+    return 0;
+  return id;
+}
+
 struct alspec_handle {
   int device;
   hipStream_t sv;        // verify stream of pipelined calls
@@ -385,7 +395,10 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   // adds no such ordering (the caller orders captured calls that share a
   // workspace): there such a wait could make a stream wait on a branch of
   // the capture that was forked from that same stream.
-  const bool cap = capturing(se) || (two && capturing(sa));
+  const unsigned long long cap_e = capture_id(se);
+  if (two && capture_id(sa) != cap_e)
+    return ALSPEC_ERR_INVALID_ARG;  // half of the call would be captured
+  const bool cap = cap_e != 0;
   bool fresh = false;
   WsEntry *ent = cap ? nullptr : ws_entry(h, ws, &fresh);
   auto wait_ws = [&](hipStream_t s) -> alspec_status {

@@ -241,7 +241,9 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
  * as for any input.
  *
  * Results are identical in all modes.  The two streams may be the same
- * stream.  `ev` may be NULL.  Buffers written by a call must not be read by
+ * stream; two distinct streams must both be outside any stream capture or
+ * in the same one (else ALSPEC_ERR_INVALID_ARG, nothing enqueued).  `ev`
+ * may be NULL.  Buffers written by a call must not be read by
  * the caller's own work until it is ordered after the call's completion on
  * the stream named above.
  */

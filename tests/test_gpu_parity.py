@@ -401,3 +401,31 @@ def test_order_after_verify_under_capture_without_pipelined_calls(handle):
         graph.replay()
     torch.cuda.synchronize()
     assert x.tolist() == [2.0] * 4
+
+
+def test_half_captured_call_rejected(handle):
+    """A fused call whose approximation stream captures while its exact
+    stream does not is refused before anything is enqueued."""
+    w = _mk("halfcap", 1, 8, 2, 128, [900], "bf16", 4, 64)
+    p = al.params_for(w, overlap=1)
+    dev = to_device(*gen.layer_inputs(w, 0))
+    ws = al.alloc_workspace(p)
+    out = al.alloc_outputs(p)
+    sa, se, cap = (torch.cuda.Stream(), torch.cuda.Stream(),
+                   torch.cuda.Stream())
+    x = torch.zeros(4, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(graph, stream=cap):
+        x.add_(1)
+        sa.wait_stream(cap)           # sa joins the capture, se does not
+        try:
+            al.spec_decode(handle, p, *dev, out, ws, sa, se)
+        except al.AlspecError as e:
+            status = e.status
+        cap.wait_stream(sa)
+    assert status == 1
+    graph.replay()
+    torch.cuda.synchronize()
+    assert x.tolist() == [1.0] * 4
