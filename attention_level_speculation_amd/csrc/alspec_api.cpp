@@ -284,13 +284,11 @@ alspec_status alspec_flash_decode_exact(alspec_handle *h,
   const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
   const float sm_log2 = p->sm_scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
-  if (include_sink_window &&
-      failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v, sm_log2,
-                                     w, s),
-             "launch_partials"))
-    return ALSPEC_ERR_HIP;
   return hip_status(
-      alspec::launch_partials(pa, p->kv_dtype, false, q, k, v, sm_log2, w, s),
+      alspec::launch_partials(pa, p->kv_dtype,
+                              include_sink_window ? alspec::kPartialsAll
+                                                  : alspec::kPartialsMiddle,
+                              q, k, v, sm_log2, w, s),
       "launch_partials");
 }
 
@@ -364,8 +362,9 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                              sm_log2, w, o, s),
                  "launch_approx_fused"))
         return ALSPEC_ERR_HIP;
-    } else if (failed(alspec::launch_partials(pa, p->kv_dtype, true, q, k, v,
-                                              sm_log2, w, s),
+    } else if (failed(alspec::launch_partials(pa, p->kv_dtype,
+                                              alspec::kPartialsApprox, q, k,
+                                              v, sm_log2, w, s),
                       "launch_partials") ||
                failed(alspec::launch_approx_combine(pa, w, o, s),
                       "launch_approx_combine")) {
@@ -376,7 +375,8 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   auto middle = [&](hipStream_t s) -> alspec_status {
     alspec_status r = record(E.exact_begin, s);
     if (r != ALSPEC_OK) return r;
-    if (failed(alspec::launch_partials(pa, p->kv_dtype, false, q, k, v,
+    if (failed(alspec::launch_partials(pa, p->kv_dtype,
+                                       alspec::kPartialsMiddle, q, k, v,
                                        sm_log2, w, s),
                "launch_partials"))
       return ALSPEC_ERR_HIP;

@@ -31,9 +31,12 @@ struct Outs {
   float lambda;
 };
 
-// Split states over the sink and window splits (approx_set = true) or the
-// middle splits, into the workspace slots.
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
+// Which splits a partials launch computes.
+enum PartialsSet { kPartialsMiddle = 0, kPartialsApprox = 1, kPartialsAll = 2 };
+
+// Split states over the sink and window splits, the middle splits, or all
+// of them (one launch), into the workspace slots.
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, PartialsSet set,
                            const float *q, const void *k, const void *v,
                            float sm_log2, const WsPtrs &w, hipStream_t s);
 

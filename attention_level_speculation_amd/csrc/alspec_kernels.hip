@@ -833,7 +833,7 @@ __device__ void group_num_den(const float *e, const float *a, float *num,
 // sink+window state merged with the middle slots, normalised into o_exact
 // (and lse_exact); each head's (num, den) of the verify goes to the
 // workspace.
-template <int D, int NH>
+template <int D, int NH, bool VERIFY = true>
 __device__ void exact_heads(const PlanArgs &pa, const WsPtrs &w, int b,
                             int h0, const float *__restrict__ o_approx,
                             float *__restrict__ o_exact,
@@ -854,11 +854,13 @@ __device__ void exact_heads(const PlanArgs &pa, const WsPtrs &w, int b,
     o_exact[bh0 * D + idx] = e;
   }
   __syncthreads();
-  group_num_den<D, NH>(r_acc, o_approx + bh0 * D, s_num, s_den);
-  __syncthreads();
+  if constexpr (VERIFY) {
+    group_num_den<D, NH>(r_acc, o_approx + bh0 * D, s_num, s_den);
+    __syncthreads();
+  }
   if (threadIdx.x < NH) {
     const int hh = threadIdx.x;
-    w.headnd[bh0 + hh] = make_float2(s_num[hh], s_den[hh]);
+    if constexpr (VERIFY) w.headnd[bh0 + hh] = make_float2(s_num[hh], s_den[hh]);
     if (lse_exact) lse_exact[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
   }
 }
@@ -928,9 +930,30 @@ __global__ __launch_bounds__(kThreads) void partials_kernel(
                             w.part_acc + ((size_t)it.slot * Hq + h0) * D);
 }
 
-// Merge of the sink and window states of entry b, kv head g into o_approx /
-// lse_approx and the reusable merged state.  The exact combine uses the
-// same merge, so with an empty middle both give the same bits.
+// Every split of the plan (sink, window and middle) in one launch: the
+// first blocks take the sink and window splits, the rest the middle ones.
+template <class KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void partials_all_kernel(
+    PlanArgs pa, const float *__restrict__ q,
+    const typename KV::elem *__restrict__ k,
+    const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w) {
+  const int nA = pa.itemA_pre[pa.B];
+  const int idx = blockIdx.x;
+  const Item it =
+      idx < nA ? decode_item(pa, true, idx) : decode_item(pa, false, idx - nA);
+  const int Hq = pa.Hq;
+  const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
+  const int h0 = it.g * G;
+  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+                            v + kv_off, it.t0, it.t1, sm_log2,
+                            w.part_ml + (size_t)it.slot * Hq + h0,
+                            w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+}
+
+// Merge of the sink and window states of entry b, kv head g into the
+// reusable merged state and (each if non-null) o_approx / lse_approx.  The
+// exact combines start from that state, so with an empty middle they give
+// the approximation's bits.
 template <int D, int G>
 __device__ void approx_merge(const PlanArgs &pa, const WsPtrs &w,
                              const Outs &o, int b, int g) {
@@ -947,7 +970,7 @@ __device__ void approx_merge(const PlanArgs &pa, const WsPtrs &w,
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D;
     w.stA_acc[bh0 * D + idx] = r_acc[idx];
-    o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
+    if (o.o_approx) o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
   }
   if (threadIdx.x < G) {
     const int hh = threadIdx.x;
@@ -1006,29 +1029,16 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
                     o.o_committed, o.lambda);
 }
 
-// Exact output from every split state of the plan; one block per
-// (entry, kv head) with the same merge as the sink+window combine, so with
-// an empty middle both give the same bits.
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void lse_combine_kernel(
+// Second stage of the exact output from every split state of the plan:
+// one block per (entry, query head) merges the head's middle states onto
+// the merged sink+window state, as the fused call's exact merge does (so
+// both give the same bits).
+template <int D>
+__global__ __launch_bounds__(kThreads) void lse_middle_kernel(
     PlanArgs pa, WsPtrs w, float *__restrict__ o_exact,
     float *__restrict__ lse_exact) {
-  __shared__ float r_acc[G * D];
-  __shared__ float r_m[G], r_l[G];
-  const int Hq = pa.Hq;
-  const int b = blockIdx.x / pa.Hkv, g = blockIdx.x % pa.Hkv;
-  const int h0 = g * G;
-  const int n = pa.nsink[b] + pa.nwin[b] + pa.nmid[b];
-  const size_t bh0 = (size_t)b * Hq + h0;
-  // no prior state; the stored-state slots only serve as valid addresses
-  merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc, pa.slot_base[b], n,
-                                  Hq, h0, false, w.stA_ml + bh0,
-                                  w.stA_acc + bh0 * D, r_acc, r_m, r_l);
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
-    o_exact[bh0 * D + idx] = normalise(r_acc[idx], r_l[idx / D]);
-  if (threadIdx.x < G && lse_exact)
-    lse_exact[bh0 + threadIdx.x] =
-        lse_nat(r_m[threadIdx.x], r_l[threadIdx.x]);
+  exact_heads<D, 1, false>(pa, w, blockIdx.x / pa.Hq, blockIdx.x % pa.Hq,
+                           nullptr, o_exact, lse_exact);
 }
 
 __global__ __launch_bounds__(kThreads) void verify_kernel(
@@ -1081,31 +1091,38 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block,
 }
 
 template <class KV, int D, int G>
-hipError_t partials_kg(const PlanArgs &pa, bool approx_set, const float *q,
+hipError_t partials_kg(const PlanArgs &pa, PartialsSet set, const float *q,
                        const void *k, const void *v, float sm_log2,
                        const WsPtrs &w, hipStream_t s) {
-  const int items = approx_set ? pa.itemA_pre[pa.B] : pa.itemM_pre[pa.B];
+  const int nA = pa.itemA_pre[pa.B], nM = pa.itemM_pre[pa.B];
+  const int items = set == kPartialsApprox   ? nA
+                    : set == kPartialsMiddle ? nM
+                                             : nA + nM;
   if (items == 0) return hipSuccess;
   using E = typename KV::elem;
-  auto kern = approx_set ? partials_kernel<KV, D, G, true>
-                         : partials_kernel<KV, D, G, false>;
-  return launch(kern, dim3(items), dim3(kThreads), s, pa, q, (const E *)k,
-                (const E *)v, sm_log2, w);
+  const dim3 grid(items), block(kThreads);
+  if (set == kPartialsAll)
+    return launch(partials_all_kernel<KV, D, G>, grid, block, s, pa, q,
+                  (const E *)k, (const E *)v, sm_log2, w);
+  auto kern = set == kPartialsApprox ? partials_kernel<KV, D, G, true>
+                                     : partials_kernel<KV, D, G, false>;
+  return launch(kern, grid, block, s, pa, q, (const E *)k, (const E *)v,
+                sm_log2, w);
 }
 
 template <class KV, int D>
-hipError_t partials_g(const PlanArgs &pa, bool approx_set, const float *q,
+hipError_t partials_g(const PlanArgs &pa, PartialsSet set, const float *q,
                       const void *k, const void *v, float sm_log2,
                       const WsPtrs &w, hipStream_t s) {
   switch (pa.G) {
     case 1:
-      return partials_kg<KV, D, 1>(pa, approx_set, q, k, v, sm_log2, w, s);
+      return partials_kg<KV, D, 1>(pa, set, q, k, v, sm_log2, w, s);
     case 2:
-      return partials_kg<KV, D, 2>(pa, approx_set, q, k, v, sm_log2, w, s);
+      return partials_kg<KV, D, 2>(pa, set, q, k, v, sm_log2, w, s);
     case 4:
-      return partials_kg<KV, D, 4>(pa, approx_set, q, k, v, sm_log2, w, s);
+      return partials_kg<KV, D, 4>(pa, set, q, k, v, sm_log2, w, s);
     case 8:
-      return partials_kg<KV, D, 8>(pa, approx_set, q, k, v, sm_log2, w, s);
+      return partials_kg<KV, D, 8>(pa, set, q, k, v, sm_log2, w, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1155,27 +1172,6 @@ hipError_t approx_combine_d(const PlanArgs &pa, const WsPtrs &w,
   return hipErrorInvalidValue;
 }
 
-template <int D>
-hipError_t lse_combine_d(const PlanArgs &pa, const WsPtrs &w, float *o_exact,
-                         float *lse_exact, hipStream_t s) {
-  dim3 grid(pa.B * pa.Hkv), block(kThreads);
-  switch (pa.G) {
-    case 1:
-      return launch(lse_combine_kernel<D, 1>, grid, block, s, pa, w, o_exact,
-                    lse_exact);
-    case 2:
-      return launch(lse_combine_kernel<D, 2>, grid, block, s, pa, w, o_exact,
-                    lse_exact);
-    case 4:
-      return launch(lse_combine_kernel<D, 4>, grid, block, s, pa, w, o_exact,
-                    lse_exact);
-    case 8:
-      return launch(lse_combine_kernel<D, 8>, grid, block, s, pa, w, o_exact,
-                    lse_exact);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 WsPtrs ws_ptrs(void *ws, const Workspace &wl) {
@@ -1190,17 +1186,17 @@ WsPtrs ws_ptrs(void *ws, const Workspace &wl) {
   return w;
 }
 
-hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, bool approx_set,
+hipError_t launch_partials(const PlanArgs &pa, int kv_dtype, PartialsSet set,
                            const float *q, const void *k, const void *v,
                            float sm_log2, const WsPtrs &w, hipStream_t s) {
   if (kv_dtype == ALSPEC_KV_BF16) {
     if (pa.D == 128)
-      return partials_g<KvBf16, 128>(pa, approx_set, q, k, v, sm_log2, w, s);
-    return partials_g<KvBf16, 64>(pa, approx_set, q, k, v, sm_log2, w, s);
+      return partials_g<KvBf16, 128>(pa, set, q, k, v, sm_log2, w, s);
+    return partials_g<KvBf16, 64>(pa, set, q, k, v, sm_log2, w, s);
   }
   if (pa.D == 128)
-    return partials_g<KvF32, 128>(pa, approx_set, q, k, v, sm_log2, w, s);
-  return partials_g<KvF32, 64>(pa, approx_set, q, k, v, sm_log2, w, s);
+    return partials_g<KvF32, 128>(pa, set, q, k, v, sm_log2, w, s);
+  return partials_g<KvF32, 64>(pa, set, q, k, v, sm_log2, w, s);
 }
 
 hipError_t launch_approx_fused(const PlanArgs &pa, int kv_dtype,
@@ -1234,8 +1230,17 @@ hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
                               float *o_exact, float *lse_exact,
                               hipStream_t s) {
-  if (pa.D == 128) return lse_combine_d<128>(pa, w, o_exact, lse_exact, s);
-  return lse_combine_d<64>(pa, w, o_exact, lse_exact, s);
+  // the sink+window state (as the approximation merges it), then the middle
+  // states on top of it
+  const Outs none{};
+  const hipError_t e = launch_approx_combine(pa, w, none, s);
+  if (e != hipSuccess) return e;
+  dim3 grid(pa.B * pa.Hq), block(kThreads);
+  if (pa.D == 128)
+    return launch(lse_middle_kernel<128>, grid, block, s, pa, w, o_exact,
+                  lse_exact);
+  return launch(lse_middle_kernel<64>, grid, block, s, pa, w, o_exact,
+                lse_exact);
 }
 
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,

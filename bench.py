@@ -25,8 +25,11 @@ Schedules (overlap modes of the library):
                 and verify between successive exact passes), as a graph.
   sequential -- every layer's approximation, exact pass and verify one
                 after another on one stream (overlap mode 0), as a graph.
-  pipelined_eager -- overlap mode 2 issued call by call without a graph
-                (host-bound: context only).
+  pipelined_eager -- overlap mode 2 issued call by call without a graph.
+  exact_only_baseline -- not speculative: exact attention over every split
+                and its merge per layer (alspec_flash_decode_exact with the
+                sink and window splits, alspec_lse_combine), as a graph;
+                reported beside the headline as the cost of speculation.
 The headline value is the throughput of the fastest of them (named in
 config.schedule); all compute the same outputs.
 
@@ -92,7 +95,7 @@ def parse_args():
     ap.add_argument("--ws-ring", type=int, default=0,
                     help="workspaces the eager pipelined schedule cycles "
                          "through (0: one per layer)")
-    ap.add_argument("--schedules", default="pipe,pipe1,seq,pipe_eager",
+    ap.add_argument("--schedules", default="pipe,pipe1,seq,pipe_eager,exact",
                     help="schedules to time (pipe is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
@@ -157,10 +160,12 @@ def main():
         return al.params_for(w0, split_tokens=args.split_tokens,
                              window_split_tokens=args.window_split_tokens,
                              overlap=overlap)
-    # schedules: name -> (overlap mode, captured as a graph)
+    # schedules: name -> (overlap mode, captured as a graph); "exact" is the
+    # non-speculative baseline: exact attention over every split, no
+    # approximation and no verify
     modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
-             "pipe_eager": (2, False)}
-    P = {m: params(ov) for m, (ov, _) in modes.items()}
+             "pipe_eager": (2, False), "exact": (None, True)}
+    P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
     mid_tokens = sum(e - b for k, b, e in splits if k == 2)
@@ -174,7 +179,7 @@ def main():
     # adds no workspace ordering under capture); the eager pipelined
     # schedule cycles through a ring, ordered by the library
     n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
-            "pipe_eager": args.ws_ring or nl}
+            "pipe_eager": args.ws_ring or nl, "exact": 1}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
     outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
@@ -196,6 +201,17 @@ def main():
                 sa.cuda_stream, se.cuda_stream]
     A = {m: [[call_args(P[m], di, l, WS[m][l % len(WS[m])])
               for l in range(nl)] for di in range(nd)] for m in modes}
+
+    def exact_args(di, layer):
+        o, ws = outs[di][layer], WS["exact"][0]
+        p = ctypes.byref(P["exact"])
+        return ([h.ptr, p, Qs[di][layer].data_ptr(), Ks[di][layer].data_ptr(),
+                 Vs[di][layer].data_ptr(), 1, ws.data_ptr(), ws.numel(),
+                 se.cuda_stream],
+                [h.ptr, p, ws.data_ptr(), ws.numel(),
+                 o["o_exact"].data_ptr(), o["lse_exact"].data_ptr(),
+                 se.cuda_stream])
+    AX = [[exact_args(di, l) for l in range(nl)] for di in range(nd)]
 
     def new_events():
         evs = {n: torch.cuda.Event(enable_timing=True) for n in EVENT_NAMES}
@@ -225,6 +241,12 @@ def main():
     def enqueue(mode, di, evrow=None):
         """One step (all layers of density di) on sa/se; evrow: per-layer
         (Events struct, dict) for instrumented runs."""
+        if mode == "exact":
+            for fa, la in AX[di]:
+                st = B_._flash_exact(*fa) or B_._lse_combine(*la)
+                if st != 0:
+                    raise al.AlspecError(st, "exact-only baseline")
+            return
         for layer in range(nl):
             if mode != "seq" and layer > 0:
                 # the approximation stream holds nothing after the previous
@@ -290,7 +312,8 @@ def main():
     for mode, key in (("pipe", "pipelined"),
                       ("pipe1", "pipelined_verify_on_exact_stream"),
                       ("seq", "sequential"),
-                      ("pipe_eager", "pipelined_eager")):
+                      ("pipe_eager", "pipelined_eager"),
+                      ("exact", "exact_only_baseline")):
         if mode not in sched:
             continue
         wall_ = timed(mode)
@@ -299,8 +322,10 @@ def main():
                     "hip_graph": modes[mode][1],
                     "ms_per_step": wall_ / args.steps * 1e3,
                     "tokens_layers_per_s": w0.B * nl * args.steps / wall_}
-    # headline: the fastest schedule (each computes the same outputs)
-    best = max(res, key=lambda k_: res[k_]["tokens_layers_per_s"])
+    # headline: the fastest speculative schedule (each computes the same
+    # outputs); the exact-only baseline is reported beside it
+    best = max((k_ for k_ in res if k_ != "exact_only_baseline"),
+               key=lambda k_: res[k_]["tokens_layers_per_s"])
     wall = res[best]["ms_per_step"] * args.steps / 1e3
 
     # ---- instrumented runs: HIP events around every kernel --------------
@@ -398,6 +423,11 @@ def main():
     }
     out["step_hbm_frac"] = out["step_kv_GBps"] / HBM_PEAK_GBPS
     out.update(res)
+    if "exact_only_baseline" in res:
+        # time a speculative step costs over exact attention alone
+        out["speculation_cost_frac"] = (
+            res[best]["ms_per_step"] /
+            res["exact_only_baseline"]["ms_per_step"] - 1.0)
     if args.kernel_launches > 0:
         us = kernel_timing(args, al, B_, h, P["seq"], Qs, Ks, Vs, se, nd, nl)
         achieved = mid_bytes / (us * 1e-6) / 1e9

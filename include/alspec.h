@@ -138,8 +138,10 @@ alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
                                  int32_t *split_tokens,
                                  int32_t *window_split_tokens);
 
-/* Create a handle bound to HIP device `device` (reads its properties and
- * creates two events for cross-stream ordering).  *out is set on success. */
+/* Create a handle bound to HIP device `device`: the events the fused call
+ * uses for cross-stream ordering, a 16-entry table of workspace events and
+ * the pipelined mode's verify stream (default priority).  *out is set on
+ * success. */
 alspec_status alspec_create(int device, alspec_handle **out);
 alspec_status alspec_destroy(alspec_handle *h);
 

@@ -70,6 +70,9 @@ def test_tiny_f32_standalone_path(handle):
     assert np.array_equal(got["o_exact"], got2["o_exact"])
     fused = run_fused(al, handle, p, qd, kd, vd)
     assert np.array_equal(fused["o_approx"], got["o_approx"])
+    # the standalone exact combine merges as the fused call does
+    assert np.array_equal(fused["o_exact"], got["o_exact"])
+    assert np.array_equal(fused["lse_exact"], got["lse_exact"])
 
 
 @pytest.mark.parametrize("layer", [0, 1])
@@ -109,6 +112,10 @@ def test_multiuser_ragged_full_size(handle):
             assert np.array_equal(seq[key], other[key]), (ov, key)
     alone = run_standalone(al, handle, al.params_for(w), qd, kd, vd)
     assert np.array_equal(alone["o_approx"], seq["o_approx"])
+    assert np.array_equal(alone["o_exact"], seq["o_exact"])
+    allsp = run_standalone(al, handle, al.params_for(w), qd, kd, vd,
+                           include_sink_window=True)
+    assert np.array_equal(allsp["o_exact"], seq["o_exact"])
 
 
 def test_llama70b_full_size(handle):
