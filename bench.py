@@ -30,6 +30,9 @@ Schedules (overlap modes of the library):
                 and its merge per layer (alspec_flash_decode_exact with the
                 sink and window splits, alspec_lse_combine), as a graph;
                 reported beside the headline as the cost of speculation.
+  static_sink_baseline -- the pages' static attention-sink baseline: the
+                approximation alone (alspec_sink_approx) as the layer's
+                output, no exact pass and no verify, as a graph.
 The headline value is the throughput of the fastest of them (named in
 config.schedule); all compute the same outputs.
 
@@ -95,7 +98,8 @@ def parse_args():
     ap.add_argument("--ws-ring", type=int, default=0,
                     help="workspaces the eager pipelined schedule cycles "
                          "through (0: one per layer)")
-    ap.add_argument("--schedules", default="pipe,pipe1,seq,pipe_eager,exact",
+    ap.add_argument("--schedules",
+                    default="pipe,pipe1,seq,pipe_eager,exact,sink",
                     help="schedules to time (pipe is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
@@ -164,7 +168,8 @@ def main():
     # non-speculative baseline: exact attention over every split, no
     # approximation and no verify
     modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
-             "pipe_eager": (2, False), "exact": (None, True)}
+             "pipe_eager": (2, False), "exact": (None, True),
+             "sink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
@@ -179,7 +184,7 @@ def main():
     # adds no workspace ordering under capture); the eager pipelined
     # schedule cycles through a ring, ordered by the library
     n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
-            "pipe_eager": args.ws_ring or nl, "exact": 1}
+            "pipe_eager": args.ws_ring or nl, "exact": 1, "sink": 1}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
     outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
@@ -212,6 +217,14 @@ def main():
                  o["o_exact"].data_ptr(), o["lse_exact"].data_ptr(),
                  se.cuda_stream])
     AX = [[exact_args(di, l) for l in range(nl)] for di in range(nd)]
+
+    def sink_args(di, layer):
+        o, ws = outs[di][layer], WS["sink"][0]
+        return [h.ptr, ctypes.byref(P["sink"]), Qs[di][layer].data_ptr(),
+                Ks[di][layer].data_ptr(), Vs[di][layer].data_ptr(),
+                o["o_approx"].data_ptr(), o["lse_approx"].data_ptr(),
+                ws.data_ptr(), ws.numel(), se.cuda_stream]
+    AS = [[sink_args(di, l) for l in range(nl)] for di in range(nd)]
 
     def new_events():
         evs = {n: torch.cuda.Event(enable_timing=True) for n in EVENT_NAMES}
@@ -246,6 +259,12 @@ def main():
                 st = B_._flash_exact(*fa) or B_._lse_combine(*la)
                 if st != 0:
                     raise al.AlspecError(st, "exact-only baseline")
+            return
+        if mode == "sink":
+            for sa_ in AS[di]:
+                st = B_._sink_approx(*sa_)
+                if st != 0:
+                    raise al.AlspecError(st, "static-sink baseline")
             return
         for layer in range(nl):
             if mode != "seq" and layer > 0:
@@ -313,7 +332,8 @@ def main():
                       ("pipe1", "pipelined_verify_on_exact_stream"),
                       ("seq", "sequential"),
                       ("pipe_eager", "pipelined_eager"),
-                      ("exact", "exact_only_baseline")):
+                      ("exact", "exact_only_baseline"),
+                      ("sink", "static_sink_baseline")):
         if mode not in sched:
             continue
         wall_ = timed(mode)
@@ -324,7 +344,7 @@ def main():
                     "tokens_layers_per_s": w0.B * nl * args.steps / wall_}
     # headline: the fastest speculative schedule (each computes the same
     # outputs); the exact-only baseline is reported beside it
-    best = max((k_ for k_ in res if k_ != "exact_only_baseline"),
+    best = max((k_ for k_ in res if not k_.endswith("_baseline")),
                key=lambda k_: res[k_]["tokens_layers_per_s"])
     wall = res[best]["ms_per_step"] * args.steps / 1e3
 
