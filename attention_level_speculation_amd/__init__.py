@@ -10,12 +10,13 @@ from ._binding import (AlspecError, Events, Handle, KV_BF16, KV_F32,
                        flash_decode_exact, last_error, lse_combine,
                        make_params,
                        order_after_verify, params_for, plan_splits,
-                       sink_approx, spec_decode, status_string, verify,
-                       version, workspace_size)
+                       sink_approx, spec_decode, spec_decode_layers,
+                       status_string, verify, version, workspace_size)
 
 __all__ = ["AlspecError", "Events", "Handle", "KV_BF16", "KV_F32",
            "LIB_PATH", "Params", "alloc_outputs", "alloc_workspace",
            "flash_decode_exact", "last_error", "lse_combine", "make_params",
            "order_after_verify", "params_for",
-           "plan_splits", "sink_approx", "spec_decode", "status_string",
+           "plan_splits", "sink_approx", "spec_decode",
+           "spec_decode_layers", "status_string",
            "verify", "version", "workspace_size"]

@@ -54,6 +54,14 @@ class Events(ctypes.Structure):
                 ("exact_begin", _P), ("exact_end", _P), ("verify_end", _P)]
 
 
+class Layer(ctypes.Structure):
+    """Mirror of alspec_layer (device pointers)."""
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o_approx", _P),
+                ("lse_approx", _P), ("o_exact", _P), ("lse_exact", _P),
+                ("ratio", _P), ("commit", _P), ("o_committed", _P),
+                ("ws", _P), ("ws_bytes", ctypes.c_size_t)]
+
+
 def _sig(name, *args):
     f = getattr(_lib, name)
     f.restype = ctypes.c_int
@@ -85,6 +93,8 @@ _lse_combine = _sig("alspec_lse_combine", _P, _PP, _P, ctypes.c_size_t, _P,
                     _P, _P)
 _verify = _sig("alspec_verify", _P, _PP, _P, _P, _P, _P, _P, _P)
 _order_after_verify = _sig("alspec_order_after_verify", _P, _P)
+_spec_decode_layers = _sig("alspec_spec_decode_layers", _P, _PP, _i32,
+                           ctypes.POINTER(Layer), _P)
 _spec_decode = _sig("alspec_spec_decode", _P, _PP, _P, _P, _P, _P, _P, _P,
                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
                     ctypes.POINTER(Events))
@@ -352,6 +362,40 @@ def spec_decode(h, p, q, k, v, out, ws, stream_approx=None,
              "o_committed", True),
         wp, wn, sa, se, ctypes.byref(ev) if ev is not None else None),
         "alspec_spec_decode")
+
+
+def layers_struct(p, layers):
+    """ctypes array of alspec_layer from (q, k, v, out, ws) tuples (out as
+    made by alloc_outputs); checks shapes and dtypes."""
+    torch = _torch()
+    B, Hq, D = p.batch, p.num_q_heads, p.head_dim
+    arr = (Layer * len(layers))()
+    for i, (q, k, v, out, ws) in enumerate(layers):
+        qp, kp, vp = _qkv(p, q, k, v)
+        wp, wn = _ws(ws)
+        arr[i] = Layer(
+            qp, kp, vp,
+            _ptr(out["o_approx"], torch.float32, (B, Hq, D), "o_approx"),
+            _ptr(out.get("lse_approx"), torch.float32, (B, Hq), "lse_approx",
+                 True),
+            _ptr(out["o_exact"], torch.float32, (B, Hq, D), "o_exact"),
+            _ptr(out.get("lse_exact"), torch.float32, (B, Hq), "lse_exact",
+                 True),
+            _ptr(out["ratio"], torch.float32, (B,), "ratio"),
+            _ptr(out["commit"], torch.uint8, (B,), "commit"),
+            _ptr(out.get("o_committed"), torch.float32, (B, Hq, D),
+                 "o_committed", True),
+            wp, wn)
+    return arr
+
+
+def spec_decode_layers(h, p, layers, stream=None):
+    """Layer-pipelined fused step over a chain of layers on one stream:
+    `layers` is a list of (q, k, v, out, ws) tuples."""
+    arr = layers_struct(p, layers)
+    _check(_spec_decode_layers(h.ptr, ctypes.byref(p), len(layers), arr,
+                               _stream(stream)),
+           "alspec_spec_decode_layers")
 
 
 def order_after_verify(h, stream=None):

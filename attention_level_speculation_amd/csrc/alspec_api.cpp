@@ -488,6 +488,65 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
   return done_ws(se);
 }
 
+alspec_status alspec_spec_decode_layers(alspec_handle *h,
+                                        const alspec_params *p,
+                                        int32_t n_layers,
+                                        const alspec_layer *layers,
+                                        void *stream) {
+  if (!h || !p || !layers || n_layers < 1) return ALSPEC_ERR_INVALID_ARG;
+  alspec::PlanArgs pa;
+  alspec::Workspace wl;
+  alspec_status st = alspec::make_plan(p, &pa, &wl);
+  if (st != ALSPEC_OK) return st;
+  for (int j = 0; j < n_layers; ++j) {
+    const alspec_layer &L = layers[j];
+    if (!L.o_approx || !L.o_exact || !L.ratio || !L.commit)
+      return ALSPEC_ERR_INVALID_ARG;
+    if ((st = check_inputs(L.q, L.k, L.v)) != ALSPEC_OK) return st;
+    if ((st = check_outputs(L.o_approx, L.o_exact, L.o_committed)) !=
+        ALSPEC_OK)
+      return st;
+    if ((st = check_ws(L.ws, L.ws_bytes, wl)) != ALSPEC_OK) return st;
+    // a workspace is in use from the launch before its layer's to the one
+    // after it
+    for (int d = 1; d <= 2 && j + d < n_layers; ++d)
+      if (layers[j + d].ws == L.ws) return ALSPEC_ERR_WORKSPACE;
+  }
+  const float sm_log2 = p->sm_scale * kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  auto chain_layer = [&](int j) {
+    const alspec_layer &L = layers[j];
+    alspec::ChainLayer c;
+    c.q = L.q;
+    c.k = L.k;
+    c.v = L.v;
+    c.w = alspec::ws_ptrs(L.ws, wl);
+    c.o = alspec::Outs{L.o_approx, L.lse_approx, L.o_exact, L.lse_exact,
+                       L.ratio,    L.commit,     L.o_committed, p->lambda};
+    return c;
+  };
+  alspec::ChainLayer first = chain_layer(0);
+  if (failed(alspec::launch_approx_fused(pa, p->kv_dtype, first.q, first.k,
+                                         first.v, sm_log2, first.w, first.o,
+                                         s),
+             "launch_approx_fused"))
+    return ALSPEC_ERR_HIP;
+  for (int j = 0; j < n_layers; ++j) {
+    const alspec::ChainLayer mid = chain_layer(j);
+    alspec::ChainLayer app{}, ver{};
+    if (j + 1 < n_layers) app = chain_layer(j + 1);
+    if (j >= 1) ver = chain_layer(j - 1);
+    if (failed(alspec::launch_chain(pa, p->kv_dtype, &mid,
+                                    j + 1 < n_layers ? &app : nullptr,
+                                    j >= 1 ? &ver : nullptr, sm_log2, s),
+               "launch_chain"))
+      return ALSPEC_ERR_HIP;
+  }
+  const alspec::ChainLayer last = chain_layer(n_layers - 1);
+  return hip_status(alspec::launch_merge_verify(pa, last.w, last.o, s),
+                    "launch_merge_verify");
+}
+
 alspec_status alspec_order_after_verify(alspec_handle *h, void *stream) {
   if (!h) return ALSPEC_ERR_INVALID_ARG;
   // The verify stream is part of a capture only after a pipelined call was

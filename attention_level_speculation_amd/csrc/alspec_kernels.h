@@ -62,6 +62,21 @@ hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
                               float *o_exact, float *lse_exact, hipStream_t s);
 
+// One layer's inputs, workspace and outputs in a layer-pipelined launch.
+struct ChainLayer {
+  const float *q;
+  const void *k, *v;
+  WsPtrs w;
+  Outs o;
+};
+
+// One layer-pipelined launch: middle splits of `mid`, the whole
+// approximation of `app` and the exact merge, verify and commit of `ver`
+// (each may be null) in one grid.
+hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
+                        const ChainLayer *mid, const ChainLayer *app,
+                        const ChainLayer *ver, float sm_log2, hipStream_t s);
+
 // Standalone verify of two output buffers.
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,
                          const float *o_exact, float *ratio, uint8_t *commit,

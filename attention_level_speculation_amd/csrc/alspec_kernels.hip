@@ -22,17 +22,16 @@
 
 #include "alspec_kernels.h"
 
+// Floating-point contraction only within one expression: a result's rounding
+// then follows from the source alone, the same in every kernel that inlines
+// a shared step.
+#pragma clang fp contract(on)
+
 namespace alspec {
 
 namespace {
 
 constexpr int kThreads = 256;
-// Tiles of K/V in flight beyond the one being computed, in the middle-split
-// loop: 1 (two register sets) or 2 (three).
-#ifndef ALSPEC_PREFETCH_DEPTH
-#define ALSPEC_PREFETCH_DEPTH 1
-#endif
-constexpr int kPrefetchDepth = ALSPEC_PREFETCH_DEPTH;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -306,60 +305,51 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// Softmax state of the G (4 or 8) query heads of one kv head over tokens
-// [t0, t1), bf16 K/V with D = 128.  The logit block S^T = K_tile Q^T of a
-// 16-token tile is one 16x16 output of v_mfma_f32_16x16x32_bf16 per
-// 32-wide slice of D (K rows are the A operand straight from HBM, the
-// query heads the B operand, padded to 16 columns).  q is split into three
-// bf16 parts whose products accumulate in fp32, so the logits keep fp32
-// accuracy.  Lane l (r = l % 16, c = l / 16) loads bytes [64c, 64c + 64) of
-// tile row r, and both operands map slice s, element j to
-// d = 32c + 8s + j.  The output gives lane l the logits of tokens 4c + j
-// (j = 0..3) for head r.  P*V runs on the VALU: lane l owns d = 8r..8r+7
-// of V rows 4c + j and reads the G probabilities of its rows from LDS.
-// Wave w takes tiles w, w + 4, ... of the range; the next tile's K and V
-// are loaded while the current one is computed.  Each wave keeps its own
-// online softmax; the waves are merged at the end.
-// QLDS keeps the q operands in LDS (read per MFMA) instead of registers,
-// and PF prefetches the next tile; without both the footprint is small
-// enough for the sink/window kernel, the merges and the middle-split kernel
-// to share a CU (the middle-split kernel uses QLDS with PF).
-template <int G, bool QLDS, bool PF>
-__device__ void split_state_mfma(const float *__restrict__ qg,
-                                 const uint16_t *__restrict__ kb,
-                                 const uint16_t *__restrict__ vb, int t0,
-                                 int t1, float sm_log2,
-                                 float2 *__restrict__ out_ml,
-                                 float *__restrict__ out_acc) {
-  static_assert(G == 4 || G == 8, "MFMA path serves groups of 4 or 8");
-  constexpr int D = 128;
-  constexpr int TILE = 16;
-  constexpr int STEP = kWaves * TILE;
+// Shared and per-wave state of the MFMA split computation below, and its
+// steps (q preparation, one tile, the split's end).
+template <int G>
+struct MfmaShared {
+  float p[kWaves][4][4][G];  // [wave][c][j][head]
+  float m[kWaves][G];
+  float l[kWaves][G];
+  float acc[kWaves][G][128];
+  bf16x8 q[3][4][64];
+};
 
-  __shared__ float s_p[kWaves][4][4][G];  // [wave][c][j][head]
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const int c = lane >> 4;
-
-  float m_lane = neg_inf();  // running max of head r (same in all 4 rows)
-  float l_lane = 0.f;        // this lane's share of head r's normaliser
+template <int G>
+struct MfmaWave {
+  static constexpr int D = 128;
+  static constexpr int TILE = 16;
+  static constexpr int STEP = kWaves * TILE;
+  int lane, wave, r, c;
+  float m_lane;  // running max of head r (same in all 4 rows)
+  float l_lane;  // this lane's share of head r's normaliser
   float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
 
-  // Rows past the range are clamped to its last row (a row of this same
-  // range, so no address outside it is formed); their logits are masked to
-  // -inf below, so they carry no weight.  Unconditional loads keep the
-  // memory pipeline free of branches.
-  const int last = t1 - 1;
-  auto load = [&](int tb, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
+  __device__ __forceinline__ void init() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    r = lane & 15;
+    c = lane >> 4;
+    reset();
+  }
+  __device__ __forceinline__ void reset() {
+    m_lane = neg_inf();
+    l_lane = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+  }
+
+  // K and V of this wave's tile at row tb.  Rows past `last` are clamped to
+  // it (a row of the same range, so no address outside it is formed);
+  // their logits are masked to -inf in tile(), so they carry no weight.
+  // Unconditional loads keep the memory pipeline free of branches.
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ kb,
+                                       const uint16_t *__restrict__ vb, int tb,
+                                       int last, u32x4 (&kk)[4],
+                                       u32x4 (&vv)[4]) const {
     const int krow = min(tb + r, last);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -369,18 +359,15 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
       const int vrow = min(tb + 4 * c + j, last);
       vv[j] = *(const u32x4 *)(vb + (size_t)vrow * D + 8 * r);
     }
-  };
+  }
 
-  // The first tile's loads go out before q is read and split, so the two
-  // round trips overlap.
-  u32x4 ka[4], va[4], kb2[4], vb2[4];
-  if (t0 < t1) load(t0 + wave * TILE, ka, va);
-
-  // q of head r (columns r >= G are padding: a valid row is read and
-  // zeroed, so the loads need no branch and go out together)
-  __shared__ bf16x8 s_q[QLDS ? 3 : 1][4][QLDS ? 64 : 1];
-  bf16x8 qh[4], qm[4], ql[4];
-  if (!QLDS || wave == 0) {
+  // q of head r into the shared operands (wave 0; columns r >= G are
+  // padding: a valid row is read and zeroed, so the loads need no branch
+  // and go out together).  The caller synchronises the block.
+  __device__ __forceinline__ void prepare_q(const float *__restrict__ qg,
+                                            float sm_log2,
+                                            MfmaShared<G> &sh) const {
+    if (wave != 0) return;
     const float4 *qr =
         (const float4 *)(qg + (size_t)(r < G ? r : G - 1) * D + 32 * c);
     const float qs = r < G ? sm_log2 : 0.f;
@@ -393,29 +380,30 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
                           qv[2 * s].z * qs,     qv[2 * s].w * qs,
                           qv[2 * s + 1].x * qs, qv[2 * s + 1].y * qs,
                           qv[2 * s + 1].z * qs, qv[2 * s + 1].w * qs};
-      split3(x, qh[s], qm[s], ql[s]);
-      if constexpr (QLDS) {
-        s_q[0][s][lane] = qh[s];
-        s_q[QLDS ? 1 : 0][s][lane] = qm[s];
-        s_q[QLDS ? 2 : 0][s][lane] = ql[s];
-      }
+      bf16x8 qh, qm, ql;
+      split3(x, qh, qm, ql);
+      sh.q[0][s][lane] = qh;
+      sh.q[1][s][lane] = qm;
+      sh.q[2][s][lane] = ql;
     }
   }
-  if constexpr (QLDS) __syncthreads();
 
-  // One 16-token tile of this wave: logits on MFMA, online softmax, P*V.
-  auto tile = [&](int tb, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
+  // One 16-token tile of this wave (rows from tb, range end t1): logits on
+  // MFMA, online softmax, P*V.
+  __device__ __forceinline__ void tile(int tb, int t1, const u32x4 (&kr)[4],
+                                       const u32x4 (&vr)[4],
+                                       MfmaShared<G> &sh) {
     // logits: lane holds tokens 4c + j of the tile for head r
     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[s]);
-      const bf16x8 b0 = QLDS ? s_q[0][s][lane] : qh[s];
-      const bf16x8 b1 = QLDS ? s_q[QLDS ? 1 : 0][s][lane] : qm[s];
-      const bf16x8 b2 = QLDS ? s_q[QLDS ? 2 : 0][s][lane] : ql[s];
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b0, a4, 0, 0, 0);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b1, a4, 0, 0, 0);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, b2, a4, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, sh.q[0][s][lane], a4,
+                                                   0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, sh.q[1][s][lane], a4,
+                                                   0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, sh.q[2][s][lane], a4,
+                                                   0, 0, 0);
     }
     float sv[4];
     float mx = neg_inf();
@@ -435,15 +423,15 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
     for (int j = 0; j < 4; ++j) {
       const float pj = fast_exp2(sv[j] - ref);
       ls += pj;
-      if (r < G) s_p[wave][c][j][r] = pj;
+      if (r < G) sh.p[wave][c][j][r] = pj;
     }
     l_lane = ls;
     // rescale: head h's factor is uniform, held by lane h
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float sh = readlane_f(sc, h);
+      const float shh = readlane_f(sc, h);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] *= sh;
+      for (int i = 0; i < 8; ++i) acc[h][i] *= shh;
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -453,7 +441,7 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
       float pv[G];
 #pragma unroll
       for (int h4 = 0; h4 < G; h4 += 4) {
-        const float4 p4 = *(const float4 *)&s_p[wave][c][j][h4];
+        const float4 p4 = *(const float4 *)&sh.p[wave][c][j][h4];
         pv[h4] = p4.x;
         pv[h4 + 1] = p4.y;
         pv[h4 + 2] = p4.z;
@@ -465,82 +453,110 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
         for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
     }
     __builtin_amdgcn_wave_barrier();
-  };
+  }
 
-  if constexpr (PF && kPrefetchDepth >= 2) {
-    // Three register sets in turn: two tiles' loads are in flight while the
-    // current one is computed; no set is copied into another, so a wait
-    // covers only the loads of the tile about to be used.
-    u32x4 kc[4], vc[4];
-    if (t0 + STEP < t1) load(t0 + STEP + wave * TILE, kb2, vb2);
-    for (int blk = t0; blk < t1; blk += 3 * STEP) {
-      const int ta = blk + wave * TILE;
-      load(ta + 2 * STEP, kc, vc);
-      tile(ta, ka, va);
-      if (blk + STEP >= t1) break;
-      load(ta + 3 * STEP, ka, va);
-      tile(ta + STEP, kb2, vb2);
-      if (blk + 2 * STEP >= t1) break;
-      load(ta + 4 * STEP, kb2, vb2);
-      tile(ta + 2 * STEP, kc, vc);
+  // The split's state: the four row groups summed (same running max in
+  // every row), then the waves merged through LDS and written out.  All
+  // threads of the block take part; on return the shared state arrays may
+  // be reused.
+  __device__ __forceinline__ void finish(MfmaShared<G> &sh,
+                                         float2 *__restrict__ out_ml,
+                                         float *__restrict__ out_acc) {
+    l_lane += __shfl_xor(l_lane, 16);
+    l_lane += __shfl_xor(l_lane, 32);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[h][i] += __shfl_xor(acc[h][i], 16);
+        acc[h][i] += __shfl_xor(acc[h][i], 32);
+      }
+    if (c == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sh.acc[wave][h][8 * r + i] = acc[h][i];
+      if (r < G) {
+        sh.m[wave][r] = m_lane;
+        sh.l[wave][r] = l_lane;
+      }
     }
-  } else if constexpr (PF) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
+      float M = neg_inf();
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
+      const float ref = exp_ref(M);
+      float ls = 0.f, a = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sw = fast_exp2(sh.m[w][h] - ref);
+        ls += sh.l[w][h] * sw;
+        a += sh.acc[w][h][d] * sw;
+      }
+      out_acc[h * D + d] = a;
+      if (d == 0) out_ml[h] = make_float2(M, ls);
+    }
+  }
+};
+
+// Softmax state of the G (4 or 8) query heads of one kv head over tokens
+// [t0, t1), bf16 K/V with D = 128.  The logit block S^T = K_tile Q^T of a
+// 16-token tile is one 16x16 output of v_mfma_f32_16x16x32_bf16 per
+// 32-wide slice of D (K rows are the A operand straight from HBM, the
+// query heads the B operand, padded to 16 columns, kept in LDS).  q is
+// split into three bf16 parts whose products accumulate in fp32, so the
+// logits keep fp32 accuracy.  Lane l (r = l % 16, c = l / 16) loads bytes
+// [64c, 64c + 64) of tile row r, and both operands map slice s, element j
+// to d = 32c + 8s + j.  The output gives lane l the logits of tokens
+// 4c + j (j = 0..3) for head r.  P*V runs on the VALU: lane l owns
+// d = 8r..8r+7 of V rows 4c + j and reads the G probabilities of its rows
+// from LDS.  Wave w takes tile w of every 64-token step of the range; with
+// PF the next tile's K and V are loaded while the current one is computed.
+// Each wave keeps its own online softmax; the waves are merged at the end.
+template <int G, bool PF>
+__device__ void split_state_mfma(const float *__restrict__ qg,
+                                 const uint16_t *__restrict__ kb,
+                                 const uint16_t *__restrict__ vb, int t0,
+                                 int t1, float sm_log2,
+                                 float2 *__restrict__ out_ml,
+                                 float *__restrict__ out_acc) {
+  static_assert(G == 4 || G == 8, "MFMA path serves groups of 4 or 8");
+  using W = MfmaWave<G>;
+  constexpr int TILE = W::TILE, STEP = W::STEP;
+  __shared__ MfmaShared<G> sh;
+  W wv;
+  wv.init();
+  const int last = t1 - 1;
+
+  // The first tile's loads go out before q is read and split, so the two
+  // round trips overlap.
+  u32x4 ka[4], va[4], kb2[4], vb2[4];
+  if (t0 < t1) wv.load(kb, vb, t0 + wv.wave * TILE, last, ka, va);
+  wv.prepare_q(qg, sm_log2, sh);
+  __syncthreads();
+
+  if constexpr (PF) {
     // Two register sets in turn: the next tile's loads are in flight while
     // the current one is computed, and no set is copied into the other, so
     // a wait covers only the loads of the tile about to be used.
     for (int blk = t0; blk < t1; blk += 2 * STEP) {
-      const int ta = blk + wave * TILE;
-      load(ta + STEP, kb2, vb2);
-      tile(ta, ka, va);
+      const int ta = blk + wv.wave * TILE;
+      wv.load(kb, vb, ta + STEP, last, kb2, vb2);
+      wv.tile(ta, t1, ka, va, sh);
       if (blk + STEP >= t1) break;
-      load(ta + 2 * STEP, ka, va);
-      tile(ta + STEP, kb2, vb2);
+      wv.load(kb, vb, ta + 2 * STEP, last, ka, va);
+      wv.tile(ta + STEP, t1, kb2, vb2, sh);
     }
   } else {
     for (int blk = t0; blk < t1; blk += STEP) {
-      const int ta = blk + wave * TILE;
-      if (blk != t0) load(ta, ka, va);
-      tile(ta, ka, va);
+      const int ta = blk + wv.wave * TILE;
+      if (blk != t0) wv.load(kb, vb, ta, last, ka, va);
+      wv.tile(ta, t1, ka, va, sh);
     }
   }
-
-  // Sum the four row groups (same running max in every row).
-  l_lane += __shfl_xor(l_lane, 16);
-  l_lane += __shfl_xor(l_lane, 32);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[h][i] += __shfl_xor(acc[h][i], 16);
-      acc[h][i] += __shfl_xor(acc[h][i], 32);
-    }
-  if (c == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s_acc[wave][h][8 * r + i] = acc[h][i];
-    if (r < G) {
-      s_m[wave][r] = m_lane;
-      s_l[wave][r] = l_lane;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float ref = exp_ref(M);
-    float ls = 0.f, a = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sw = fast_exp2(s_m[w][h] - ref);
-      ls += s_l[w][h] * sw;
-      a += s_acc[w][h][d] * sw;
-    }
-    out_acc[h * D + d] = a;
-    if (d == 0) out_ml[h] = make_float2(M, ls);
-  }
+  wv.finish(sh, out_ml, out_acc);
 }
 
 // ------------------------------------------------------- merge of splits ---
@@ -780,8 +796,7 @@ __device__ __forceinline__ void split_any(const float *qg,
                                           float2 *out_ml, float *out_acc) {
   if constexpr (std::is_same<KV, KvBf16>::value && D == 128 &&
                 (G == 4 || G == 8))
-    split_state_mfma<G, true, PF>(qg, kb, vb, t0, t1, sm_log2, out_ml,
-                                  out_acc);
+    split_state_mfma<G, PF>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
   else
     split_state<KV, D, G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
 }
@@ -1033,6 +1048,58 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
 // one block per (entry, query head) merges the head's middle states onto
 // the merged sink+window state, as the fused call's exact merge does (so
 // both give the same bits).
+// Layer-pipelined launch: one grid holds three disjoint block ranges, all
+// resident at once (three 4-wave blocks fit a CU):
+//   [0, nA)              the whole approximation of layer j+1, one block
+//                        per sink or window split, the last of an (entry,
+//                        kv head) to finish merging the group's states,
+//   [nA, nA + nM)        the middle splits of layer j,
+//   [nA + nM, ...)       merge, verify and commit of layer j-1.
+// Launch order alone then carries every dependency of the speculative
+// chain: layer j+1's approximation follows layer j's (one launch earlier),
+// layer j's middle splits follow the approximation of layer j-1, and layer
+// j-1's verify follows its middle splits and approximation.  The short
+// approximation blocks are dispatched first and are done within the first
+// quarter of the launch.  Giving each group's splits to fewer blocks, in
+// turn, spares the device-scope hand-off but made the launch longer: a
+// block's splits run one after another at the streaming blocks' pace.
+template <class KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void chain_kernel(
+    PlanArgs pa, ChainLayer mid, ChainLayer app, ChainLayer ver, int nM,
+    int nA, float sm_log2) {
+  using E = typename KV::elem;
+  const int Hq = pa.Hq;
+  int idx = blockIdx.x;
+  if (idx >= nA + nM) {
+    idx -= nA + nM;
+    const int b = idx / Hq, h = idx % Hq;
+    exact_heads<D, 1>(pa, ver.w, b, h, ver.o.o_approx, ver.o.o_exact,
+                      ver.o.lse_exact);
+    if (!arrive_last(ver.w.counters + kUserCounters + b, (unsigned)Hq))
+      return;
+    finalize_entry<D>(pa, ver.w, b, ver.o.o_approx, ver.o.o_exact,
+                      ver.o.ratio, ver.o.commit, ver.o.o_committed,
+                      ver.o.lambda);
+    return;
+  }
+  const bool approx = idx < nA;
+  const ChainLayer &L = approx ? app : mid;
+  const Item it = decode_item(pa, approx, approx ? idx : idx - nA);
+  const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
+  const int h0 = it.g * G;
+  split_any<KV, D, G, true>(L.q + ((size_t)it.b * Hq + h0) * D,
+                            (const E *)L.k + kv_off, (const E *)L.v + kv_off,
+                            it.t0, it.t1, sm_log2,
+                            L.w.part_ml + (size_t)it.slot * Hq + h0,
+                            L.w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+  if (!approx) return;
+  const unsigned n = (unsigned)(pa.nsink[it.b] + pa.nwin[it.b]);
+  if (!arrive_last(app.w.counters + kApproxCounters + it.b * pa.Hkv + it.g,
+                   n))
+    return;
+  approx_merge<D, G>(pa, app.w, app.o, it.b, it.g);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void lse_middle_kernel(
     PlanArgs pa, WsPtrs w, float *__restrict__ o_exact,
@@ -1172,7 +1239,49 @@ hipError_t approx_combine_d(const PlanArgs &pa, const WsPtrs &w,
   return hipErrorInvalidValue;
 }
 
+template <class KV, int D, int G>
+hipError_t chain_kg(const PlanArgs &pa, const ChainLayer *mid,
+                    const ChainLayer *app, const ChainLayer *ver,
+                    float sm_log2, hipStream_t s) {
+  const ChainLayer none{};
+  const int nV = ver ? pa.B * pa.Hq : 0;
+  const int nA = app ? pa.itemA_pre[pa.B] : 0;
+  const int nM = mid ? pa.itemM_pre[pa.B] : 0;
+  if (nV + nA + nM == 0) return hipSuccess;
+  return launch(chain_kernel<KV, D, G>, dim3(nV + nA + nM), dim3(kThreads), s,
+                pa, mid ? *mid : none, app ? *app : none, ver ? *ver : none,
+                nM, nA, sm_log2);
+}
+
+template <class KV, int D>
+hipError_t chain_g(const PlanArgs &pa, const ChainLayer *mid,
+                   const ChainLayer *app, const ChainLayer *ver, float sm_log2,
+                   hipStream_t s) {
+  switch (pa.G) {
+    case 1:
+      return chain_kg<KV, D, 1>(pa, mid, app, ver, sm_log2, s);
+    case 2:
+      return chain_kg<KV, D, 2>(pa, mid, app, ver, sm_log2, s);
+    case 4:
+      return chain_kg<KV, D, 4>(pa, mid, app, ver, sm_log2, s);
+    case 8:
+      return chain_kg<KV, D, 8>(pa, mid, app, ver, sm_log2, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
+                        const ChainLayer *mid, const ChainLayer *app,
+                        const ChainLayer *ver, float sm_log2, hipStream_t s) {
+  if (kv_dtype == ALSPEC_KV_BF16) {
+    if (pa.D == 128) return chain_g<KvBf16, 128>(pa, mid, app, ver, sm_log2, s);
+    return chain_g<KvBf16, 64>(pa, mid, app, ver, sm_log2, s);
+  }
+  if (pa.D == 128) return chain_g<KvF32, 128>(pa, mid, app, ver, sm_log2, s);
+  return chain_g<KvF32, 64>(pa, mid, app, ver, sm_log2, s);
+}
 
 WsPtrs ws_ptrs(void *ws, const Workspace &wl) {
   char *base = (char *)ws;

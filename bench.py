@@ -26,6 +26,12 @@ Schedules (overlap modes of the library):
   sequential -- every layer's approximation, exact pass and verify one
                 after another on one stream (overlap mode 0), as a graph.
   pipelined_eager -- overlap mode 2 issued call by call without a graph.
+  layer_pipelined -- alspec_spec_decode_layers on one stream: launch j runs
+                layer j's exact split-K pass, layer j+1's approximation
+                and layer j-1's merge/verify/commit as disjoint block
+                ranges of one grid; stream order carries the speculative
+                dependencies.  Three workspaces in a ring.  Issued eagerly,
+                and (layer_pipelined_graph) as a graph.
   exact_only_baseline -- not speculative: exact attention over every split
                 and its merge per layer (alspec_flash_decode_exact with the
                 sink and window splits, alspec_lse_combine), as a graph;
@@ -99,7 +105,8 @@ def parse_args():
                     help="workspaces the eager pipelined schedule cycles "
                          "through (0: one per layer)")
     ap.add_argument("--schedules",
-                    default="pipe,pipe1,seq,pipe_eager,exact,sink",
+                    default="pipe,pipe1,seq,pipe_eager,chain,chain_graph,"
+                            "exact,sink",
                     help="schedules to time (pipe is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
@@ -168,7 +175,8 @@ def main():
     # non-speculative baseline: exact attention over every split, no
     # approximation and no verify
     modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
-             "pipe_eager": (2, False), "exact": (None, True),
+             "pipe_eager": (2, False), "chain": (None, False),
+             "chain_graph": (None, True), "exact": (None, True),
              "sink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
@@ -184,7 +192,8 @@ def main():
     # adds no workspace ordering under capture); the eager pipelined
     # schedule cycles through a ring, ordered by the library
     n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
-            "pipe_eager": args.ws_ring or nl, "exact": 1, "sink": 1}
+            "pipe_eager": args.ws_ring or nl, "chain": 3, "chain_graph": 3,
+            "exact": 1, "sink": 1}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
     outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
@@ -226,6 +235,12 @@ def main():
                 ws.data_ptr(), ws.numel(), se.cuda_stream]
     AS = [[sink_args(di, l) for l in range(nl)] for di in range(nd)]
 
+    # layer-pipelined chains: one alspec_layer array per (schedule, density)
+    AC = {m: [B_.layers_struct(P[m], [
+        (Qs[di][l], Ks[di][l], Vs[di][l], outs[di][l], WS[m][l % 3])
+        for l in range(nl)]) for di in range(nd)]
+        for m in ("chain", "chain_graph")}
+
     def new_events():
         evs = {n: torch.cuda.Event(enable_timing=True) for n in EVENT_NAMES}
         for ev_ in evs.values():
@@ -259,6 +274,12 @@ def main():
                 st = B_._flash_exact(*fa) or B_._lse_combine(*la)
                 if st != 0:
                     raise al.AlspecError(st, "exact-only baseline")
+            return
+        if mode in ("chain", "chain_graph"):
+            st = B_._spec_decode_layers(h.ptr, ctypes.byref(P[mode]), nl,
+                                        AC[mode][di], se.cuda_stream)
+            if st != 0:
+                raise al.AlspecError(st, "alspec_spec_decode_layers")
             return
         if mode == "sink":
             for sa_ in AS[di]:
@@ -332,6 +353,8 @@ def main():
                       ("pipe1", "pipelined_verify_on_exact_stream"),
                       ("seq", "sequential"),
                       ("pipe_eager", "pipelined_eager"),
+                      ("chain", "layer_pipelined"),
+                      ("chain_graph", "layer_pipelined_graph"),
                       ("exact", "exact_only_baseline"),
                       ("sink", "static_sink_baseline")):
         if mode not in sched:

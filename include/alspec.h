@@ -258,6 +258,46 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  size_t ws_bytes, void *stream_approx,
                                  void *stream_exact, const alspec_events *ev);
 
+/* One layer's buffers for alspec_spec_decode_layers: as the arguments of
+ * alspec_spec_decode (device pointers; lse_approx, lse_exact and
+ * o_committed may be NULL). */
+typedef struct {
+  const float *q;
+  const void *k, *v;
+  float *o_approx, *lse_approx, *o_exact, *lse_exact, *ratio;
+  uint8_t *commit;
+  float *o_committed;
+  void *ws;
+  size_t ws_bytes;
+} alspec_layer;
+
+/*
+ * The fused step for a chain of n_layers layers of one decode step, on one
+ * stream, layer-pipelined: the speculative order ("run the post-attention
+ * ops speculatively ... while exact attention is computed",
+ * atlas.scime.ai summary, Approach), with layer l+1's query taken to be
+ * available once layer l's approximation is.  Launch 0 computes layer 0's
+ * approximation; launch j (j = 0..n-1) computes, in disjoint block ranges
+ * of one grid, layer j's middle splits, layer j+1's approximation and
+ * layer j-1's exact merge, verify and commit; a last launch verifies layer
+ * n-1.  Stream order alone carries the dependencies, so successive exact
+ * passes run back to back with no event or cross-stream wait between
+ * them.  Each layer's outputs equal those of alspec_spec_decode (any
+ * mode) on its inputs, bit for bit.  p->overlap is ignored.
+ *
+ * `layers` is a host array of n_layers entries (>= 1), each validated as
+ * the arguments of alspec_spec_decode.  Entries whose layers are fewer
+ * than 3 apart must not share a workspace (ALSPEC_ERR_WORKSPACE); from 3
+ * apart they may (a ring of three workspaces serves any chain).  Calls
+ * sharing a workspace with other calls are ordered by the caller.  May be
+ * captured into a HIP graph.
+ */
+alspec_status alspec_spec_decode_layers(alspec_handle *h,
+                                        const alspec_params *p,
+                                        int32_t n_layers,
+                                        const alspec_layer *layers,
+                                        void *stream);
+
 /* Orders `stream` after all merge, verify and commit work that pipelined
  * calls (p->overlap == 2) on this handle have enqueued so far.  Under
  * stream capture: joins the handle's verify stream back into the capture

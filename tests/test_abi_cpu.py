@@ -156,3 +156,30 @@ def test_workspace_grows_with_splits():
 
 def test_last_error_is_a_string():
     assert isinstance(al.last_error(), str)
+
+
+def test_layers_chain_validation_before_gpu_work():
+    """alspec_spec_decode_layers rejects bad arguments and workspaces shared
+    by layers fewer than 3 apart before any HIP call (no GPU needed)."""
+    p = P()
+    f = _binding._spec_decode_layers
+    fake_h = ctypes.c_void_p(0x1000)
+    assert f(None, ctypes.byref(p), 1, None, None) == 1
+    arr = (_binding.Layer * 4)()
+    assert f(fake_h, ctypes.byref(p), 0, arr, None) == 1
+    size = al.workspace_size(p)
+    base = 1 << 40                        # aligned stand-in addresses
+    for i in range(4):
+        arr[i] = _binding.Layer(base, base, base, base, None, base, None,
+                                base, base, None, base + (i << 30), size)
+    arr[2].ws = arr[1].ws                 # layers 1 and 2 share
+    assert f(fake_h, ctypes.byref(p), 4, arr, None) == 3
+    arr[2].ws = base + (2 << 30)
+    arr[3].ws = arr[1].ws                 # layers 1 and 3 share
+    assert f(fake_h, ctypes.byref(p), 4, arr, None) == 3
+    arr[3].ws = base + (3 << 30)
+    arr[1].ws_bytes = size - 1            # too small
+    assert f(fake_h, ctypes.byref(p), 4, arr, None) == 3
+    arr[1].ws_bytes = size
+    arr[2].q = base + 4                   # misaligned input
+    assert f(fake_h, ctypes.byref(p), 4, arr, None) == 1

@@ -436,3 +436,77 @@ def test_half_captured_call_rejected(handle):
     graph.replay()
     torch.cuda.synchronize()
     assert x.tolist() == [1.0] * 4
+
+
+def _chain(handle, w, n_layers, n_ws=3, lam=None):
+    lam = w.lam if lam is None else lam
+    p = al.params_for(w, lam=lam)
+    devs = [to_device(*gen.layer_inputs(w, l)) for l in range(n_layers)]
+    wss = [al.alloc_workspace(p) for _ in range(n_ws)]
+    outs = [al.alloc_outputs(p) for _ in range(n_layers)]
+    return p, devs, wss, outs
+
+
+@pytest.mark.parametrize("shape,n_layers", [
+    ("bf16_g4", 1), ("bf16_g4", 2), ("bf16_g4", 5), ("f32_g2", 4),
+    ("bf16_g8_ragged", 3)])
+def test_layers_chain_matches_single_calls(handle, shape, n_layers):
+    """The layer-pipelined chain gives every layer exactly the outputs of a
+    single fused call on its inputs, with a ring of three workspaces."""
+    w = {"bf16_g4": gen.scaled(gen.llama8b_32k(), 6000),
+         "f32_g2": _mk("c2", 2, 8, 4, 128, [2500, 777], "f32", 4, 256),
+         "bf16_g8_ragged": _mk("c8", 3, 16, 2, 128, [3000, 130, 5000],
+                               "bf16", 4, 128)}[shape]
+    print(f"[case] chain {shape} layers={n_layers}", flush=True)
+    p, devs, wss, outs = _chain(handle, w, n_layers)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3])
+                                      for j, (d, o) in enumerate(zip(devs,
+                                                                     outs))],
+                          s)
+    torch.cuda.synchronize()
+    for j, d in enumerate(devs):
+        ref = run_fused(al, handle, p, *d)
+        for key in ref:
+            assert np.array_equal(outs[j][key].cpu().numpy(), ref[key]), \
+                (j, key)
+    # and against the oracle for the last layer
+    q, k, v = gen.layer_inputs(w, n_layers - 1)
+    ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam)
+    compare({k_: v_.cpu().numpy() for k_, v_ in outs[-1].items()}, ref,
+            w.kv_dtype, w.lam, "chain-last")
+
+
+def test_layers_chain_graph_replays(handle):
+    """A captured chain replays to the eager chain's outputs, three times,
+    with eager chains on the same workspaces between replays."""
+    w = gen.scaled(gen.llama8b_32k(), 5000)
+    p, devs, wss, outs = _chain(handle, w, 4)
+    eager = [al.alloc_outputs(p) for _ in devs]
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o) in
+                                      enumerate(zip(devs, eager))])
+    torch.cuda.synchronize()
+    want = [{k_: v_.cpu().numpy() for k_, v_ in o.items()} for o in eager]
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+                                          in enumerate(zip(devs, outs))],
+                              cap)
+    for rep in range(3):
+        for o in outs:
+            for t in o.values():
+                t.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            graph.replay()
+        torch.cuda.synchronize()
+        for j, o in enumerate(outs):
+            for key in want[j]:
+                assert np.array_equal(o[key].cpu().numpy(), want[j][key]), \
+                    (rep, j, key)
+        al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+                                          in enumerate(zip(devs, eager))])
+        torch.cuda.synchronize()
