@@ -32,6 +32,9 @@ namespace alspec {
 namespace {
 
 constexpr int kThreads = 256;
+// Register sets for K/V tiles per wave in the MFMA split loop (the tiles in
+// flight while one is computed are one fewer).
+constexpr int kPrefetchSets = 2;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -512,10 +515,12 @@ struct MfmaWave {
 // to d = 32c + 8s + j.  The output gives lane l the logits of tokens
 // 4c + j (j = 0..3) for head r.  P*V runs on the VALU: lane l owns
 // d = 8r..8r+7 of V rows 4c + j and reads the G probabilities of its rows
-// from LDS.  Wave w takes tile w of every 64-token step of the range; with
-// PF the next tile's K and V are loaded while the current one is computed.
+// from LDS.  Wave w takes tile w of every 64-token step of the range and
+// keeps NS register sets for K and V in turn: the loads of the next NS - 1
+// tiles are in flight while one is computed, and no set is copied into
+// another, so a wait covers only the loads of the tile about to be used.
 // Each wave keeps its own online softmax; the waves are merged at the end.
-template <int G, bool PF>
+template <int G, int NS>
 __device__ void split_state_mfma(const float *__restrict__ qg,
                                  const uint16_t *__restrict__ kb,
                                  const uint16_t *__restrict__ vb, int t0,
@@ -523,37 +528,34 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
                                  float2 *__restrict__ out_ml,
                                  float *__restrict__ out_acc) {
   static_assert(G == 4 || G == 8, "MFMA path serves groups of 4 or 8");
+  static_assert(NS >= 2, "at least one tile in flight");
   using W = MfmaWave<G>;
   constexpr int TILE = W::TILE, STEP = W::STEP;
   __shared__ MfmaShared<G> sh;
   W wv;
   wv.init();
   const int last = t1 - 1;
+  const int ta0 = t0 + wv.wave * TILE;  // this wave's tile i is at ta0 + i*STEP
 
-  // The first tile's loads go out before q is read and split, so the two
-  // round trips overlap.
-  u32x4 ka[4], va[4], kb2[4], vb2[4];
-  if (t0 < t1) wv.load(kb, vb, t0 + wv.wave * TILE, last, ka, va);
+  // The first tiles' loads go out before q is read and split, so the round
+  // trips overlap.  Rows past the range are clamped to its last row.
+  u32x4 kr[NS][4], vr[NS][4];
+  if (t0 < t1) {
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
+  }
   wv.prepare_q(qg, sm_log2, sh);
   __syncthreads();
 
-  if constexpr (PF) {
-    // Two register sets in turn: the next tile's loads are in flight while
-    // the current one is computed, and no set is copied into the other, so
-    // a wait covers only the loads of the tile about to be used.
-    for (int blk = t0; blk < t1; blk += 2 * STEP) {
-      const int ta = blk + wv.wave * TILE;
-      wv.load(kb, vb, ta + STEP, last, kb2, vb2);
-      wv.tile(ta, t1, ka, va, sh);
-      if (blk + STEP >= t1) break;
-      wv.load(kb, vb, ta + 2 * STEP, last, ka, va);
-      wv.tile(ta + STEP, t1, kb2, vb2, sh);
-    }
-  } else {
-    for (int blk = t0; blk < t1; blk += STEP) {
-      const int ta = blk + wv.wave * TILE;
-      if (blk != t0) wv.load(kb, vb, ta, last, ka, va);
-      wv.tile(ta, t1, ka, va, sh);
+  for (int blk = t0; blk < t1; blk += NS * STEP) {
+    const int ta = blk + wv.wave * TILE;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      wv.load(kb, vb, ta + (i + NS - 1) * STEP, last, kr[(i + NS - 1) % NS],
+              vr[(i + NS - 1) % NS]);
+      wv.tile(ta + i * STEP, t1, kr[i], vr[i], sh);
+      if (i + 1 < NS && blk + (i + 1) * STEP >= t1) break;
     }
   }
   wv.finish(sh, out_ml, out_acc);
@@ -788,7 +790,7 @@ constexpr int kMergeRoundA = 8;
 // ... and in the exact merges (many middle splits).
 constexpr int kMergeRoundM = 8;
 
-template <class KV, int D, int G, bool PF>
+template <class KV, int D, int G>
 __device__ __forceinline__ void split_any(const float *qg,
                                           const typename KV::elem *kb,
                                           const typename KV::elem *vb, int t0,
@@ -796,7 +798,8 @@ __device__ __forceinline__ void split_any(const float *qg,
                                           float2 *out_ml, float *out_acc) {
   if constexpr (std::is_same<KV, KvBf16>::value && D == 128 &&
                 (G == 4 || G == 8))
-    split_state_mfma<G, PF>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
+    split_state_mfma<G, kPrefetchSets>(qg, kb, vb, t0, t1, sm_log2, out_ml,
+                                       out_acc);
   else
     split_state<KV, D, G>(qg, kb, vb, t0, t1, sm_log2, out_ml, out_acc);
 }
@@ -939,7 +942,7 @@ __global__ __launch_bounds__(kThreads) void partials_kernel(
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+  split_any<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
                             v + kv_off, it.t0, it.t1, sm_log2,
                             w.part_ml + (size_t)it.slot * Hq + h0,
                             w.part_acc + ((size_t)it.slot * Hq + h0) * D);
@@ -959,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void partials_all_kernel(
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+  split_any<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
                             v + kv_off, it.t0, it.t1, sm_log2,
                             w.part_ml + (size_t)it.slot * Hq + h0,
                             w.part_acc + ((size_t)it.slot * Hq + h0) * D);
@@ -1010,7 +1013,7 @@ __global__ __launch_bounds__(kThreads) void approx_fused_kernel(
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G, true>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
+  split_any<KV, D, G>(q + ((size_t)it.b * Hq + h0) * D, k + kv_off,
                             v + kv_off, it.t0, it.t1, sm_log2,
                             w.part_ml + (size_t)it.slot * Hq + h0,
                             w.part_acc + ((size_t)it.slot * Hq + h0) * D);
@@ -1087,7 +1090,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
   const Item it = decode_item(pa, approx, approx ? idx : idx - nA);
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
-  split_any<KV, D, G, true>(L.q + ((size_t)it.b * Hq + h0) * D,
+  split_any<KV, D, G>(L.q + ((size_t)it.b * Hq + h0) * D,
                             (const E *)L.k + kv_off, (const E *)L.v + kv_off,
                             it.t0, it.t1, sm_log2,
                             L.w.part_ml + (size_t)it.slot * Hq + h0,

@@ -18,13 +18,6 @@ int pow2_floor(int x) {
   return r;
 }
 
-// Power of two nearest to x (ties up).
-int pow2_near(int64_t x) {
-  int r = 1;
-  while ((int64_t)r * 2 <= x) r *= 2;
-  return (x - r >= (int64_t)2 * r - x) ? 2 * r : r;
-}
-
 }  // namespace
 
 alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
@@ -62,7 +55,6 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
   pa->L_cap = p->kv_capacity;
 
   // Sets of every entry.
-  int64_t mid_tokens = 0;
   int max_win = 0;
   for (int b = 0; b < B; ++b) {
     const int L = p->seq_lens[b];
@@ -72,20 +64,41 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     pa->L[b] = L;
     pa->s_end[b] = s_end;
     pa->w_begin[b] = (int)wb;
-    mid_tokens += ((int)wb - s_end) * (int64_t)Hkv;
     if (L - (int)wb > max_win) max_win = L - (int)wb;
   }
 
-  // Middle split length: about two work items per CU, so one wave of
-  // resident blocks covers the whole pass (no tail), with long splits whose
-  // per-split state is a small share of the bytes and whose merge is short.
+  // Middle split length: the shortest whole number of 64-token steps (at
+  // least 256 tokens) whose splits number no more than one per CU, or one
+  // per CU-round when the (entry, kv head) pairs alone outnumber the CUs.
+  // With one split per CU every CU streams from start to end; with two or
+  // more per CU the block dispatched first runs ahead of the others (the
+  // wave arbiter favours older waves) and the CU streams its last stretch
+  // with fewer loads in flight.
   int T = p->split_tokens;
   if (T == 0) {
-    const int64_t target_items = (int64_t)2 * kNominalCUs;
-    int64_t t = mid_tokens / target_items;
-    if (t < 256) t = 256;
-    if (t > 8192) t = 8192;
-    T = pow2_near(t);
+    int pairs = 0, max_mid = 0;
+    for (int b = 0; b < B; ++b) {
+      const int m = pa->w_begin[b] - pa->s_end[b];
+      if (m > 0) pairs += Hkv;
+      if (m > max_mid) max_mid = m;
+    }
+    const int64_t target =
+        (int64_t)kNominalCUs * ((pairs + kNominalCUs - 1) / kNominalCUs);
+    auto items = [&](int64_t t) {
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b) {
+        const int64_t m = pa->w_begin[b] - pa->s_end[b];
+        if (m > 0) n += Hkv * ((m + t - 1) / t);
+      }
+      return n;
+    };
+    int64_t lo = 4, hi = (max_mid + 63) / 64;  // in 64-token steps
+    if (hi < lo) hi = lo;
+    while (lo < hi) {                          // smallest fitting length
+      const int64_t mid = (lo + hi) / 2;
+      if (items(mid * 64) <= target) hi = mid; else lo = mid + 1;
+    }
+    T = (int)(lo * 64);
   }
   // Window split length: the window is on the approximation's latency path,
   // so it is cut into about 16 pieces that run side by side.

@@ -139,13 +139,44 @@ def test_split_plan_tiles_context(seed):
 
 def test_headline_plan_shape():
     """Context 131072, S 4, W 2048, 8 kv heads: one sink split, window cut
-    into 16 pieces of 128, middle pieces of 2048 (about two items per CU)."""
+    into 16 pieces of 128, middle pieces of 4032 tokens: 32 per kv head,
+    one per CU."""
     p = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1)
     splits, (T, Tw) = al.plan_splits(p, 0)
-    assert Tw == 128 and T == 2048
+    assert Tw == 128 and T == 4032
     assert sum(1 for s in splits if s[0] == 1) == 16
-    assert sum(1 for s in splits if s[0] == 2) == 63
+    assert sum(1 for s in splits if s[0] == 2) == 32
     _check_tiling(p, 0, 131072, 4, 2048)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_middle_split_length_fills_the_cus_once(seed):
+    """The default middle split length is the shortest whole number of
+    64-token steps, at least 256, whose splits over all entries and kv heads
+    number at most one per CU (256), or per round of 256 when the (entry,
+    kv head) pairs with a middle outnumber the CUs."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 65))
+    Hkv = int(rng.choice([1, 2, 4, 8, 16]))
+    L_cap = int(rng.choice([3000, 20000, 131072]))
+    lens = [int(x) for x in rng.integers(1, L_cap + 1, size=B)]
+    S, W = 4, int(rng.choice([64, 2048]))
+    p = al.make_params(B, Hkv * 4, Hkv, 128, L_cap, lens, "bf16", S, W, 0.1)
+    T = al.plan_splits(p, 0)[1][0]
+    mids = [max(0, max(min(S, L), L - W) - min(S, L)) for L in lens]
+
+    def items(t):
+        return Hkv * sum(-(-m // t) for m in mids if m > 0)
+    pairs = Hkv * sum(1 for m in mids if m > 0)
+    target = 256 * -(-pairs // 256)
+    assert T % 64 == 0 and T >= 256
+    if pairs:
+        assert items(T) <= target
+        if T > 256:
+            assert items(T - 64) > target
+    got = sum(1 for b in range(B) for s in al.plan_splits(p, b)[0]
+              if s[0] == 2)
+    assert got * Hkv == items(T)
 
 
 def test_workspace_grows_with_splits():
