@@ -42,10 +42,12 @@ Schedules (overlap modes of the library):
 The headline value is the throughput of the fastest of them (named in
 config.schedule); all compute the same outputs.
 
-Also reported: KV GB/s of the exact split-K kernel against the HBM peak
-(HIP events on its stream around back-to-back launches of it over all
-resident layers), per-kernel HIP events in eagerly issued steps of the
-schedules, the speculation
+Also reported: KV GB/s of the headline schedule's dominant kernel against
+the HBM peak (for the layer-pipelined schedules its kernel in the steady
+state, from HIP events around back-to-back chains of all layers and of two;
+beside it the exact split-K kernel alone, from HIP events around
+back-to-back launches over all resident layers), per-kernel HIP events in
+eagerly issued steps of the schedules, the speculation
 hit rate per density, each layer's time to its approximate and to its
 verified output and the critical-path time a commit saves, the HBM probe,
 and the CPU oracle timed on a bounded sample of the same layers.
@@ -67,29 +69,34 @@ HBM_PEAK_GBPS = 8000.0
 EVENT_NAMES = ("approx_begin", "approx_end", "exact_begin", "exact_end",
                "verify_end")
 
-# HBM bytes per launch of the exact split-K kernel on this workload, from
+# HBM bytes per launch of each roofline kernel on this workload, from
 # rocprofv3 FETCH_SIZE and WRITE_SIZE runs, scaled by what the counters read
 # for a copy kernel of known size (fetch x2.000, write x1.000).  Valid only
-# for the kernel sources they were taken on (sha256 of the files below);
-# once those change the figure is withheld until measured again.
+# for the kernel and plan sources they were taken on (sha256 of the files
+# below); once those change the figures are withheld until measured again.
 TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip",
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
-                       "attention_level_speculation_amd/csrc/alspec_plan.h"),
-           "sha256": "78dd6c6993024be1264d4ffcf7c1cc35"
-                     "4bd984d8ae106739bff9daaf21a53fa8",
-           "fetch_bytes": 258222.3 * 1024 * 2.0,
-           "write_bytes": 1023.8 * 1024 * 1.0}
+                       "attention_level_speculation_amd/csrc/alspec_plan.h",
+                       "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
+           "sha256": "1569207038c4b4997edc955e79635935"
+                     "b43db958ba0e1c66184aed191ac38fe0",
+           # (fetch, write) per launch; the chain kernel's in its steady
+           # state (all three block ranges)
+           "bytes": {"chain": (262901.8 * 1024 * 2.0, 870.3 * 1024 * 1.0),
+                     "partials_middle": (258204.5 * 1024 * 2.0,
+                                         520.0 * 1024 * 1.0)}}
 
 
-def measured_traffic():
+def measured_traffic(kernel):
     import hashlib
     h = hashlib.sha256()
     for rel in TRAFFIC["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    if h.hexdigest() != TRAFFIC["sha256"]:
+    if h.hexdigest() != TRAFFIC["sha256"] or kernel not in TRAFFIC["bytes"]:
         return None
-    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    fetch, write = TRAFFIC["bytes"][kernel]
+    return fetch + write
 
 
 def parse_args():
@@ -107,12 +114,13 @@ def parse_args():
     ap.add_argument("--schedules",
                     default="pipe,pipe1,seq,pipe_eager,chain,chain_graph,"
                             "exact,sink",
-                    help="schedules to time (pipe is the headline)")
+                    help="schedules to time (the fastest is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
     ap.add_argument("--kernel-launches", type=int, default=768,
-                    help="back-to-back launches of the exact split-K kernel "
-                         "timed for the roofline (0: skip)")
+                    help="back-to-back launches timed for the roofline: of "
+                         "the exact split-K kernel, and about as many of the "
+                         "layer-pipelined kernel (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
@@ -323,8 +331,6 @@ def main():
         return g
 
     torch.cuda.synchronize()
-    if "pipe" not in args.schedules.split(","):
-        sys.exit("the pipelined schedule (pipe) is the headline; keep it")
     graphs = {m: [capture(m, di) for di in range(nd)]
               for m, (_, g) in modes.items()
               if g and m in args.schedules.split(",")}
@@ -471,20 +477,41 @@ def main():
         out["speculation_cost_frac"] = (
             res[best]["ms_per_step"] /
             res["exact_only_baseline"]["ms_per_step"] - 1.0)
+    # ---- roofline: the dominant kernel of the headline schedule ---------
+    # (the layer-pipelined kernel for the chain schedules, else the exact
+    # split-K kernel), and the exact split-K kernel alone beside it
     if args.kernel_launches > 0:
         us = kernel_timing(args, al, B_, h, P["seq"], Qs, Ks, Vs, se, nd, nl)
         achieved = mid_bytes / (us * 1e-6) / 1e9
-        out["roofline"] = {
+        exact_pass = {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic("partials_middle"),
             "kernel": "partials_kernel<KvBf16,128,4,false> (exact split-K "
                       "pass over the middle)",
             "algorithmic_bytes_per_launch": mid_bytes,
             "launch_us_mean": us,
             "launches_timed": args.kernel_launches,
-            "approx_tokens_per_head": a_tokens,
         }
+        if best in ("layer_pipelined", "layer_pipelined_graph"):
+            cus, reps = chain_timing(args, B_, h, P["chain"], AC["chain"], se,
+                                     nl)
+            achieved = layer_bytes / (cus * 1e-6) / 1e9
+            out["roofline"] = {
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": measured_traffic("chain"),
+                "kernel": "chain_kernel<KvBf16,128,4> (steady state: "
+                          "approximation of layer j+1, middle splits of "
+                          "layer j, verify of layer j-1)",
+                "algorithmic_bytes_per_launch": layer_bytes,
+                "launch_us_mean": cus,
+                "launches_timed": reps * nd * (nl - 2),
+            }
+            out["roofline_exact_pass"] = exact_pass
+        else:
+            out["roofline"] = exact_pass
+        out["roofline"]["approx_tokens_per_head"] = a_tokens
 
     # ---- CPU oracle baseline --------------------------------------------
     if not args.no_cpu_baseline:
@@ -501,9 +528,10 @@ def main():
         torch.cuda.empty_cache()
         pr = sdev.probe_bandwidth()
         out["probe"] = {k: round(v["GBps"], 1) for k, v in pr.items()}
-        if "roofline" in out:
-            out["roofline"]["frac_of_probe_read"] = (
-                out["roofline"]["achieved"] / pr["read"]["GBps"])
+        for key in ("roofline", "roofline_exact_pass"):
+            if key in out:
+                out[key]["frac_of_probe_read"] = (
+                    out[key]["achieved"] / pr["read"]["GBps"])
 
     print(json.dumps(out), flush=True)
     h.close()
@@ -537,6 +565,45 @@ def kernel_timing(args, al, B_, h, p, Qs, Ks, Vs, stream, nd, nl):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / args.kernel_launches
+
+
+def chain_timing(args, B_, h, p, arrs, stream, nl):
+    """Average duration of the layer-pipelined kernel in its steady state
+    (approximation of layer j+1, middle splits of layer j, verify of layer
+    j-1 in one launch).  alspec_spec_decode_layers runs back to back over
+    all nl layers and, separately, over the first two, each bracketed by
+    two HIP events on the stream it runs on; both hold one first and one
+    last launch plus the chain's lone first approximation and last verify,
+    so the difference of the two per-call times over nl - 2 is one
+    steady-state launch (inter-launch gaps count against it).  Returns
+    (microseconds, repetitions per density)."""
+    import torch
+    if nl < 3:
+        raise SystemExit("the chain's steady state needs at least 3 layers")
+    two = [(B_.Layer * 2)(a[0], a[1]) for a in arrs]
+
+    def run(layers, n, reps):
+        for _ in range(reps):
+            for arr in layers:
+                st = B_._spec_decode_layers(h.ptr, ctypes.byref(p), n, arr,
+                                            stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"alspec_spec_decode_layers: {st}")
+    reps = max(1, args.kernel_launches // (len(arrs) * nl))
+    torch.cuda.synchronize()
+    run(arrs, nl, 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    run(arrs, nl, reps)
+    ev[1].record(stream)
+    ev[2].record(stream)
+    run(two, 2, reps)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    n = reps * len(arrs)
+    full = ev[0].elapsed_time(ev[1]) * 1e3 / n
+    short = ev[2].elapsed_time(ev[3]) * 1e3 / n
+    return (full - short) / (nl - 2), reps
 
 
 def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
