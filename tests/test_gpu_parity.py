@@ -478,6 +478,37 @@ def test_layers_chain_matches_single_calls(handle, shape, n_layers):
             w.kv_dtype, w.lam, "chain-last")
 
 
+@pytest.mark.parametrize("shape,n_layers", [("llama8b_128k", 4),
+                                             ("llama70b_128k", 3)])
+def test_layers_chain_full_size(handle, shape, n_layers):
+    """The chain at full size with the automatic plan, the configuration
+    the benchmark times (a launch with all three block ranges from the
+    third layer on): every layer against the oracle, and bit for bit
+    against single fused calls on its inputs."""
+    w = {"llama8b_128k": gen.llama8b_128k(needles=4),
+         "llama70b_128k": gen.llama70b_128k()}[shape]
+    p = al.params_for(w)
+    print(f"[case] chain full size {shape} layers={n_layers}", flush=True)
+    devs, refs = [], []
+    for layer in range(n_layers):
+        q, k, v = gen.layer_inputs(w, layer)
+        refs.append(oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam))
+        devs.append(to_device(q, k, v))
+        del q, k, v
+    wss = [al.alloc_workspace(p) for _ in range(3)]
+    outs = [al.alloc_outputs(p) for _ in range(n_layers)]
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+                                      in enumerate(zip(devs, outs))])
+    torch.cuda.synchronize()
+    for j, d in enumerate(devs):
+        got = {k_: v_.cpu().numpy() for k_, v_ in outs[j].items()}
+        compare(got, refs[j], w.kv_dtype, w.lam, f"{shape} chain layer {j}")
+        single = run_fused(al, handle, p, *d)
+        for key in single:
+            assert np.array_equal(got[key], single[key]), (j, key)
+        print(f"[case] layer {j} ratio {got['ratio'][:4]}", flush=True)
+
+
 def test_layers_chain_graph_replays(handle):
     """A captured chain replays to the eager chain's outputs, three times,
     with eager chains on the same workspaces between replays."""
