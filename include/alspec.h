@@ -83,8 +83,16 @@ typedef struct {
   int32_t window;       /* W >= 0, S + W >= 1 */
   float sm_scale;       /* logit scale, > 0 and finite (normally 1/sqrt(D)) */
   float lambda;         /* verify threshold, >= 0 (+inf allowed, NaN not) */
-  int32_t split_tokens;        /* middle split length; 0 = automatic */
-  int32_t window_split_tokens; /* window split length; 0 = automatic */
+  int32_t split_tokens;        /* middle split length; 0 = automatic: the
+                                  shortest multiple of 64 tokens (at least
+                                  256) giving at most one middle split per
+                                  CU of an MI355X (256), or per round of
+                                  256 when the (entry, kv head) pairs are
+                                  more.  Results depend on the split plan
+                                  only through rounding order. */
+  int32_t window_split_tokens; /* window split length; 0 = automatic: about
+                                  1/16 of the longest window, a power of
+                                  two in [64, 512] */
   int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
                       2 = pipelined (see alspec_spec_decode) */
 } alspec_params;
