@@ -78,12 +78,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "1569207038c4b4997edc955e79635935"
-                     "b43db958ba0e1c66184aed191ac38fe0",
+           "sha256": "02a70ff9742afc5a027d30298abf5deb"
+                     "778688b9187e943c3d6ebd9ba79391bc",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262901.8 * 1024 * 2.0, 870.3 * 1024 * 1.0),
-                     "partials_middle": (258204.5 * 1024 * 2.0,
+           "bytes": {"chain": (262902.0 * 1024 * 2.0, 871.3 * 1024 * 1.0),
+                     "partials_middle": (258200.0 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
