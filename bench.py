@@ -39,8 +39,13 @@ Schedules (overlap modes of the library):
   static_sink_baseline -- the pages' static attention-sink baseline: the
                 approximation alone (alspec_sink_approx) as the layer's
                 output, no exact pass and no verify, as a graph.
-The headline value is the throughput of the fastest of them (named in
-config.schedule); all compute the same outputs.
+  fixed_layer_sink_baseline -- the pages' attention sink at fixed layers:
+                the static approximation on the odd layers, exact attention
+                (as in the exact-only baseline) on the even ones, as a graph.
+The headline value is the throughput of the fastest speculative schedule
+(named in config.schedule); those all compute the same outputs.  The
+baselines are reported beside it, with each one's output error against
+exact attention on the same inputs.
 
 Also reported: KV GB/s of the headline schedule's dominant kernel against
 the HBM peak (for the layer-pipelined schedules its kernel in the steady
@@ -113,7 +118,7 @@ def parse_args():
                          "through (0: one per layer)")
     ap.add_argument("--schedules",
                     default="pipe,pipe1,seq,pipe_eager,chain,chain_graph,"
-                            "exact,sink",
+                            "exact,sink,fixsink",
                     help="schedules to time (the fastest is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
@@ -185,7 +190,7 @@ def main():
     modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
              "pipe_eager": (2, False), "chain": (None, False),
              "chain_graph": (None, True), "exact": (None, True),
-             "sink": (None, True)}
+             "sink": (None, True), "fixsink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
@@ -201,7 +206,7 @@ def main():
     # schedule cycles through a ring, ordered by the library
     n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
             "pipe_eager": args.ws_ring or nl, "chain": 3, "chain_graph": 3,
-            "exact": 1, "sink": 1}
+            "exact": 1, "sink": 1, "fixsink": 1}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
     outs = [[al.alloc_outputs(P["seq"], dev) for _ in range(nl)]
@@ -295,6 +300,16 @@ def main():
                 if st != 0:
                     raise al.AlspecError(st, "static-sink baseline")
             return
+        if mode == "fixsink":
+            for layer in range(nl):
+                if layer % 2:
+                    st = B_._sink_approx(*AS[di][layer])
+                else:
+                    fa, la = AX[di][layer]
+                    st = B_._flash_exact(*fa) or B_._lse_combine(*la)
+                if st != 0:
+                    raise al.AlspecError(st, "fixed-layer sink baseline")
+            return
         for layer in range(nl):
             if mode != "seq" and layer > 0:
                 # the approximation stream holds nothing after the previous
@@ -362,7 +377,8 @@ def main():
                       ("chain", "layer_pipelined"),
                       ("chain_graph", "layer_pipelined_graph"),
                       ("exact", "exact_only_baseline"),
-                      ("sink", "static_sink_baseline")):
+                      ("sink", "static_sink_baseline"),
+                      ("fixsink", "fixed_layer_sink_baseline")):
         if mode not in sched:
             continue
         wall_ = timed(mode)
@@ -436,6 +452,30 @@ def main():
         allc += c
     hit_rate = sum(allc) / len(allc)
 
+    # ---- output error against exact attention (same inputs) -------------
+    # per (user, layer), the relative L2 error of the layer's attention
+    # output: the verify's ratio where the approximation stands, 0 where
+    # exact attention does.  The pages score tasks, which synthetic inputs
+    # cannot; this is the error the verify bounds.
+    ratio = np.array([[outs[di][layer]["ratio"].cpu().numpy()
+                       for layer in range(nl)] for di in range(nd)])
+    commit = np.array([[outs[di][layer]["commit"].cpu().numpy()
+                        for layer in range(nl)] for di in range(nd)]) != 0
+    odd = (np.arange(nl) % 2 == 1)[None, :, None]
+
+    def err_stats(e):
+        return {"mean": float(e.mean()), "max": float(e.max()),
+                "frac_over_lambda": float((e > w0.lam).mean())}
+    quality = {
+        "measure": "relative L2 error of the attention output against "
+                   "exact attention, per (user, layer), over every "
+                   "density and layer",
+        "speculative": err_stats(np.where(commit, ratio, 0.0)),
+        "static_sink_baseline": err_stats(ratio),
+        "fixed_layer_sink_baseline": err_stats(np.where(odd, ratio, 0.0)),
+        "exact_only_baseline": err_stats(np.zeros_like(ratio)),
+    }
+
     out = {
         "metric": METRIC,
         "value": w0.B * nl * args.steps / wall,
@@ -467,6 +507,7 @@ def main():
         },
         "hit_rate": hit_rate,
         "hit_rate_by_needles": hits,
+        "output_error": quality,
         "kv_bytes_per_layer": layer_bytes,
         "step_kv_GBps": layer_bytes * nl * args.steps / wall / 1e9,
     }
