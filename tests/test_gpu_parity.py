@@ -449,14 +449,21 @@ def _chain(handle, w, n_layers, n_ws=3, lam=None):
 
 @pytest.mark.parametrize("shape,n_layers", [
     ("bf16_g4", 1), ("bf16_g4", 2), ("bf16_g4", 5), ("f32_g2", 4),
-    ("bf16_g8_ragged", 3)])
+    ("bf16_g8_ragged", 3), ("f32_d64_g1_ragged", 4),
+    ("bf16_d64_g4_tiny", 3)])
 def test_layers_chain_matches_single_calls(handle, shape, n_layers):
     """The layer-pipelined chain gives every layer exactly the outputs of a
-    single fused call on its inputs, with a ring of three workspaces."""
+    single fused call on its inputs, with a ring of three workspaces: MFMA
+    and VALU split kernels, head dims 128 and 64, users whose context is
+    shorter than the sink plus window (no middle) or a single token."""
     w = {"bf16_g4": gen.scaled(gen.llama8b_32k(), 6000),
          "f32_g2": _mk("c2", 2, 8, 4, 128, [2500, 777], "f32", 4, 256),
          "bf16_g8_ragged": _mk("c8", 3, 16, 2, 128, [3000, 130, 5000],
-                               "bf16", 4, 128)}[shape]
+                               "bf16", 4, 128),
+         "f32_d64_g1_ragged": _mk("c1", 3, 4, 4, 64, [1777, 90, 2600],
+                                  "f32", 4, 100),
+         "bf16_d64_g4_tiny": _mk("c4", 4, 8, 2, 64, [1, 2049, 5, 300],
+                                 "bf16", 4, 128)}[shape]
     print(f"[case] chain {shape} layers={n_layers}", flush=True)
     p, devs, wss, outs = _chain(handle, w, n_layers)
     s = torch.cuda.Stream()
