@@ -403,3 +403,81 @@ def order_after_verify(h, stream=None):
     pipelined calls on handle `h` have enqueued."""
     _check(_order_after_verify(h.ptr, _stream(stream)),
            "alspec_order_after_verify")
+
+
+# ------------------------------------------------ post-attention operators ---
+
+POST_MAX_BATCH = 8
+
+
+class PostParams(ctypes.Structure):
+    """Mirror of alspec_post_params."""
+    _fields_ = [("batch", _i32), ("attn_dim", _i32), ("hidden", _i32),
+                ("ffn", _i32), ("qkv_dim", _i32), ("eps", ctypes.c_float)]
+
+
+class PostWeights(ctypes.Structure):
+    """Mirror of alspec_post_weights (device pointers to bf16 weights)."""
+    _fields_ = [("w_o", _P), ("norm_mlp", _P), ("w_gate", _P), ("w_up", _P),
+                ("w_down", _P), ("norm_attn", _P), ("w_qkv", _P)]
+
+
+POST_WEIGHT_NAMES = ("w_o", "norm_mlp", "w_gate", "w_up", "w_down",
+                     "norm_attn", "w_qkv")
+
+_post_workspace_size = _sig("alspec_post_workspace_size",
+                            ctypes.POINTER(PostParams),
+                            ctypes.POINTER(ctypes.c_size_t))
+_post_attention = _sig("alspec_post_attention", _P,
+                       ctypes.POINTER(PostParams),
+                       ctypes.POINTER(PostWeights), _P, _P, _P, _P, _P, _P,
+                       ctypes.c_size_t, _P)
+
+
+def make_post_params(batch, attn_dim, hidden, ffn, qkv_dim, eps=1e-5):
+    return PostParams(int(batch), int(attn_dim), int(hidden), int(ffn),
+                      int(qkv_dim), float(eps))
+
+
+def post_workspace_size(p):
+    n = ctypes.c_size_t()
+    _check(_post_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "alspec_post_workspace_size")
+    return n.value
+
+
+def alloc_post_workspace(p, device="cuda"):
+    """Device workspace of alspec_post_attention (256-byte aligned)."""
+    torch = _torch()
+    n = post_workspace_size(p)
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def post_weights_struct(p, w):
+    """alspec_post_weights from a dict of bf16 device tensors."""
+    torch = _torch()
+    shapes = {"w_o": (p.hidden, p.attn_dim), "norm_mlp": (p.hidden,),
+              "w_gate": (p.ffn, p.hidden), "w_up": (p.ffn, p.hidden),
+              "w_down": (p.hidden, p.ffn), "norm_attn": (p.hidden,),
+              "w_qkv": (p.qkv_dim, p.hidden)}
+    return PostWeights(*[_ptr(w[n], torch.bfloat16, shapes[n], n)
+                         for n in POST_WEIGHT_NAMES])
+
+
+def post_attention(h, p, w, o, h_in, h_out, qkv, ws, skip=None, stream=None):
+    """Post-attention operators (alspec_post_attention); `w` is a dict of
+    bf16 device tensors or a PostWeights struct."""
+    torch = _torch()
+    B = p.batch
+    ws_struct = w if isinstance(w, PostWeights) else post_weights_struct(p, w)
+    wp, wn = _ws(ws)
+    _check(_post_attention(
+        h.ptr, ctypes.byref(p), ctypes.byref(ws_struct),
+        _ptr(o, torch.float32, (B, p.attn_dim), "o"),
+        _ptr(h_in, torch.float32, (B, p.hidden), "h_in"),
+        _ptr(h_out, torch.float32, (B, p.hidden), "h_out"),
+        _ptr(qkv, torch.float32, (B, p.qkv_dim), "qkv"),
+        _ptr(skip, torch.uint8, (B,), "skip", True), wp, wn, _stream(stream)),
+        "alspec_post_attention")

@@ -6,7 +6,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libalspec.so")
-SOURCES = ["alspec_kernels.hip", "alspec_api.cpp", "alspec_plan.cpp"]
+SOURCES = ["alspec_kernels.hip", "alspec_post.hip", "alspec_api.cpp",
+           "alspec_plan.cpp"]
 
 # Packed fp32 instructions stay off (the compiler would otherwise form them
 # from plain float code).

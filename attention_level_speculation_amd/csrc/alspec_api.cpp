@@ -570,3 +570,76 @@ alspec_status alspec_order_after_verify(alspec_handle *h, void *stream) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ post-attention ---
+
+namespace {
+
+alspec_status check_post(const alspec_post_params *p) {
+  if (!p) return ALSPEC_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->attn_dim < 8 || p->hidden < 8 || p->ffn < 8 ||
+      p->qkv_dim < 1)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (p->attn_dim % 8 || p->hidden % 8 || p->ffn % 8)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (!(p->eps > 0.f) || !std::isfinite(p->eps)) return ALSPEC_ERR_INVALID_ARG;
+  if (p->batch > ALSPEC_POST_MAX_BATCH) return ALSPEC_ERR_UNSUPPORTED;
+  return ALSPEC_OK;
+}
+
+size_t post_ws_bytes(const alspec_post_params *p) {
+  return alspec::align_up((size_t)p->batch * p->ffn * 4, alspec::kWsAlign);
+}
+
+}  // namespace
+
+alspec_status alspec_post_workspace_size(const alspec_post_params *p,
+                                         size_t *bytes) {
+  if (!bytes) return ALSPEC_ERR_INVALID_ARG;
+  const alspec_status st = check_post(p);
+  if (st != ALSPEC_OK) return st;
+  *bytes = post_ws_bytes(p);
+  return ALSPEC_OK;
+}
+
+alspec_status alspec_post_attention(alspec_handle *h,
+                                    const alspec_post_params *p,
+                                    const alspec_post_weights *w,
+                                    const float *o, const float *h_in,
+                                    float *h_out, float *qkv,
+                                    const uint8_t *skip, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  if (!h || !w) return ALSPEC_ERR_INVALID_ARG;
+  alspec_status st = check_post(p);
+  if (st != ALSPEC_OK) return st;
+  const void *ptrs[] = {w->w_o,    w->norm_mlp,  w->w_gate, w->w_up,
+                        w->w_down, w->norm_attn, w->w_qkv,  o,
+                        h_in,      h_out,        qkv};
+  for (const void *q : ptrs)
+    if (!q || !aligned(q, 16)) return ALSPEC_ERR_INVALID_ARG;
+  if (skip && h_out == h_in) return ALSPEC_ERR_INVALID_ARG;
+  if ((const void *)h_out == (const void *)o ||
+      (const void *)h_out == (const void *)qkv)
+    return ALSPEC_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, alspec::kWsAlign)) return ALSPEC_ERR_WORKSPACE;
+  if (ws_bytes < post_ws_bytes(p)) return ALSPEC_ERR_WORKSPACE;
+  alspec::PostShape sh{p->batch, p->attn_dim, p->hidden, p->ffn, p->qkv_dim,
+                       p->eps};
+  alspec::PostPtrs pp{};
+  pp.w_o = (const uint16_t *)w->w_o;
+  pp.norm_mlp = (const uint16_t *)w->norm_mlp;
+  pp.w_gate = (const uint16_t *)w->w_gate;
+  pp.w_up = (const uint16_t *)w->w_up;
+  pp.w_down = (const uint16_t *)w->w_down;
+  pp.norm_attn = (const uint16_t *)w->norm_attn;
+  pp.w_qkv = (const uint16_t *)w->w_qkv;
+  pp.o = o;
+  pp.h_in = h_in;
+  pp.h_out = h_out;
+  pp.qkv = qkv;
+  pp.m = (float *)ws;
+  pp.skip = skip;
+  return hip_status(
+      alspec::launch_post_attention(sh, pp, (hipStream_t)stream),
+      "launch_post_attention");
+}

@@ -82,4 +82,25 @@ hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,
                          const float *o_exact, float *ratio, uint8_t *commit,
                          float *o_committed, float lambda, hipStream_t s);
 
+// Shape of the post-attention operators (validated by the caller).
+struct PostShape {
+  int batch, attn_dim, hidden, ffn, qkv_dim;
+  float eps;
+};
+
+// Buffers of the post-attention operators: bf16 weights (uint16 bits),
+// fp32 activations, optional skip flags ([batch], nonzero: leave that
+// entry's outputs untouched).
+struct PostPtrs {
+  const uint16_t *w_o, *norm_mlp, *w_gate, *w_up, *w_down, *norm_attn, *w_qkv;
+  const float *o, *h_in;
+  float *h_out, *qkv, *m;  // m: [batch][ffn] scratch
+  const uint8_t *skip;
+};
+
+// Output projection with residual, RMSNorm + gated MLP, down projection
+// with residual, RMSNorm + next layer's QKV: four launches on `s`.
+hipError_t launch_post_attention(const PostShape &sh, const PostPtrs &p,
+                                 hipStream_t s);
+
 }  // namespace alspec

@@ -1,0 +1,351 @@
+// Post-attention operators of one decoder layer for a decode token per
+// batch entry, the work that attention-level speculation runs early on the
+// approximate attention output ("Attention-Level Speculation", research-map
+// page, summary and Approach: the post-attention ops run speculatively
+// while exact attention is computed).  The operators follow the Llama
+// decoder layer that the pages' 8B and 70B shapes name, with random bf16
+// weights:
+//   h1  = h_in + W_o o                             (output projection)
+//   m   = silu(W_gate x) * (W_up x),  x = rmsnorm(h1) * g_mlp
+//   h2  = h1 + W_down m
+//   qkv = W_qkv y,  y = rmsnorm(h2) * g_attn        (next layer's input)
+// with rmsnorm(v) = v / sqrt(mean(v^2) + eps).
+//
+// Every product is a skinny matrix-vector product (B <= 8 rows of
+// activations against a bf16 weight matrix read once), so each kernel is
+// bound by HBM bandwidth: 2 bytes per weight for B fused multiply-adds.
+// One wave owns kRows consecutive weight rows and walks the shared
+// dimension K in 16-byte chunks (8 bf16), lane l taking chunks l, l + 64,
+// ...; U chunks per row are loaded before any is used, so about 16 KiB per
+// wave is in flight.  The activations are read from L2 (they are a few KiB
+// and shared by every wave).  The row sums are reduced across the wave by
+// butterflies in a fixed order, so results do not depend on timing.
+//
+// The RMSNorm is folded into the products: sum_k W[n][k] (v[k] r g[k]) =
+// r * sum_k W[n][k] (v[k] g[k]), and each wave accumulates sum_k v[k]^2
+// from the same chunks it multiplies, so no separate pass or kernel
+// computes the norm.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <tuple>
+
+#include "alspec_kernels.h"
+
+#pragma clang fp contract(on)
+
+namespace alspec {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 4;  // weight rows per wave
+
+__device__ __forceinline__ void unpack_bf16(const uint4 r, float *f) {
+  // A bf16 is the high half of the float32 with the same value.
+  f[0] = __uint_as_float(r.x << 16);
+  f[1] = __uint_as_float(r.x & 0xffff0000u);
+  f[2] = __uint_as_float(r.y << 16);
+  f[3] = __uint_as_float(r.y & 0xffff0000u);
+  f[4] = __uint_as_float(r.z << 16);
+  f[5] = __uint_as_float(r.z & 0xffff0000u);
+  f[6] = __uint_as_float(r.w << 16);
+  f[7] = __uint_as_float(r.w & 0xffff0000u);
+}
+
+// True when entry b's outputs are to be written (no skip flags, or its
+// flag is zero).
+__device__ __forceinline__ bool active(const uint8_t *skip, int b) {
+  return skip == nullptr || skip[b] == 0;
+}
+
+template <int B>
+__device__ __forceinline__ bool any_active(const uint8_t *skip) {
+  if (skip == nullptr) return true;
+  bool any = false;
+#pragma unroll
+  for (int b = 0; b < B; ++b) any = any || skip[b] == 0;
+  return any;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Row sums acc[m][r][b] = sum_k W_m[n0 + r][k] * x[b][k] * (g[k] if G)
+// over k in [0, K), for NW weight matrices sharing rows n0 .. n0+kRows-1
+// (rows past `nrows` repeat the last valid row and are not written by the
+// callers).  With G, ss[b] = sum_k x[b][k]^2.  Sums are complete in every
+// lane on return.
+template <int B, int NW, bool G>
+__device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
+                                          int nrows, int K,
+                                          const float *__restrict__ x,
+                                          const uint16_t *__restrict__ g,
+                                          float (&acc)[NW][kRows][B],
+                                          float (&ss)[B]) {
+  constexpr int U = 4 / NW;  // chunks per row in flight
+  const int lane = threadIdx.x & 63;
+  const int nchunk = K >> 3;
+#pragma unroll
+  for (int m = 0; m < NW; ++m)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[m][r][b] = 0.f;
+#pragma unroll
+  for (int b = 0; b < B; ++b) ss[b] = 0.f;
+  const uint16_t *rowp[NW][kRows];
+#pragma unroll
+  for (int m = 0; m < NW; ++m)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+      rowp[m][r] = W[m] + (size_t)(n0 + min(r, nrows - 1)) * K;
+
+  for (int c0 = 0; c0 < nchunk; c0 += 64 * U) {
+    uint4 wv[NW][kRows][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + u * 64 + lane, nchunk - 1);
+#pragma unroll
+      for (int m = 0; m < NW; ++m)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+          wv[m][r][u] = *(const uint4 *)(rowp[m][r] + (size_t)c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nchunk) {
+        float gs[8];
+        if constexpr (G) unpack_bf16(*(const uint4 *)(g + (size_t)c * 8), gs);
+        float wf[NW][kRows][8];
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) unpack_bf16(wv[m][r][u], wf[m][r]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float4 xa = *(const float4 *)(x + (size_t)b * K + c * 8);
+          const float4 xb = *(const float4 *)(x + (size_t)b * K + c * 8 + 4);
+          float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          if constexpr (G) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              ss[b] += xv[i] * xv[i];
+              xv[i] *= gs[i];
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < NW; ++m)
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[m][r][b] += wf[m][r][i] * xv[i];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NW; ++m)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[m][r][b] = wave_sum(acc[m][r][b]);
+  if constexpr (G) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = wave_sum(ss[b]);
+  }
+}
+
+struct PostArgsK {
+  int N, K;
+  float eps;
+  const uint16_t *w0, *w1;  // weight matrices [N][K]
+  const uint16_t *g;        // norm weight [K] (norm kernels)
+  const float *x;           // activations [B][K]
+  const float *base;        // residual [B][N] (residual kernels)
+  float *y;                 // output [B][N]
+  const uint8_t *skip;      // [B] or null
+};
+
+// y[b][n] = base[b][n] + sum_k W[n][k] x[b][k]   (output and down
+// projections; y may alias base).
+template <int B>
+__global__ __launch_bounds__(kThreads) void gemv_residual_kernel(PostArgsK a) {
+  if (!any_active<B>(a.skip)) return;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int n0 = wave * kRows;
+  if (n0 >= a.N) return;
+  const int nrows = min(kRows, a.N - n0);
+  const uint16_t *W[1] = {a.w0};
+  float acc[1][kRows][B], ss[B];
+  wave_rows<B, 1, false>(W, n0, nrows, a.K, a.x, nullptr, acc, ss);
+  const int lane = threadIdx.x & 63;
+  if (lane < kRows * B) {
+    const int r = lane / B, b = lane % B;
+    float v = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb)
+        if (rr == r && bb == b) v = acc[0][rr][bb];
+    if (r < nrows && active(a.skip, b)) {
+      const size_t i = (size_t)b * a.N + n0 + r;
+      a.y[i] = a.base[i] + v;
+    }
+  }
+}
+
+// m[b][n] = silu(r_b gate) * (r_b up), gate/up = sum_k W_{gate,up}[n][k]
+// x[b][k] g[k], r_b = 1 / sqrt(mean_k x[b][k]^2 + eps).
+template <int B>
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(PostArgsK a) {
+  if (!any_active<B>(a.skip)) return;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int n0 = wave * kRows;
+  if (n0 >= a.N) return;
+  const int nrows = min(kRows, a.N - n0);
+  const uint16_t *W[2] = {a.w0, a.w1};
+  float acc[2][kRows][B], ss[B];
+  wave_rows<B, 2, true>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  const int lane = threadIdx.x & 63;
+  if (lane < kRows * B) {
+    const int r = lane / B, b = lane % B;
+    float gv = 0.f, uv = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb)
+        if (rr == r && bb == b) {
+          gv = acc[0][rr][bb];
+          uv = acc[1][rr][bb];
+        }
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+      if (bb == b) s2 = ss[bb];
+    if (r < nrows && active(a.skip, b)) {
+      const float rn = 1.f / sqrtf(s2 / (float)a.K + a.eps);
+      gv *= rn;
+      uv *= rn;
+      a.y[(size_t)b * a.N + n0 + r] = gv / (1.f + expf(-gv)) * uv;
+    }
+  }
+}
+
+// y[b][n] = r_b sum_k W[n][k] x[b][k] g[k]   (next layer's QKV).
+template <int B>
+__global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
+  if (!any_active<B>(a.skip)) return;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int n0 = wave * kRows;
+  if (n0 >= a.N) return;
+  const int nrows = min(kRows, a.N - n0);
+  const uint16_t *W[1] = {a.w0};
+  float acc[1][kRows][B], ss[B];
+  wave_rows<B, 1, true>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  const int lane = threadIdx.x & 63;
+  if (lane < kRows * B) {
+    const int r = lane / B, b = lane % B;
+    float v = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb)
+        if (rr == r && bb == b) v = acc[0][rr][bb];
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+      if (bb == b) s2 = ss[bb];
+    if (r < nrows && active(a.skip, b))
+      a.y[(size_t)b * a.N + n0 + r] = v / sqrtf(s2 / (float)a.K + a.eps);
+  }
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_k(void (*kern)(KArgs...), int n_rows, hipStream_t s,
+                    Args &&...args) {
+  const int waves = (n_rows + kRows - 1) / kRows;
+  const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
+  std::tuple<KArgs...> t(std::forward<Args>(args)...);
+  void *argv[sizeof...(KArgs)];
+  std::apply([&](auto &...e) {
+    int i = 0;
+    ((argv[i++] = (void *)&e), ...);
+  }, t);
+  return hipLaunchKernel((const void *)kern, grid, block, argv, 0, s);
+}
+
+template <int B>
+hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
+  PostArgsK a{};
+  a.eps = sh.eps;
+  a.skip = p.skip;
+  // h1 = h_in + W_o o, into h_out
+  a.N = sh.hidden;
+  a.K = sh.attn_dim;
+  a.w0 = p.w_o;
+  a.x = p.o;
+  a.base = p.h_in;
+  a.y = p.h_out;
+  hipError_t e = launch_k(gemv_residual_kernel<B>, a.N, s, a);
+  if (e != hipSuccess) return e;
+  // m = silu(gate) * up over rmsnorm(h1) * g_mlp
+  a = PostArgsK{};
+  a.eps = sh.eps;
+  a.skip = p.skip;
+  a.N = sh.ffn;
+  a.K = sh.hidden;
+  a.w0 = p.w_gate;
+  a.w1 = p.w_up;
+  a.g = p.norm_mlp;
+  a.x = p.h_out;
+  a.y = p.m;
+  e = launch_k(gate_up_kernel<B>, a.N, s, a);
+  if (e != hipSuccess) return e;
+  // h2 = h1 + W_down m, in place
+  a = PostArgsK{};
+  a.eps = sh.eps;
+  a.skip = p.skip;
+  a.N = sh.hidden;
+  a.K = sh.ffn;
+  a.w0 = p.w_down;
+  a.x = p.m;
+  a.base = p.h_out;
+  a.y = p.h_out;
+  e = launch_k(gemv_residual_kernel<B>, a.N, s, a);
+  if (e != hipSuccess) return e;
+  // qkv = W_qkv (rmsnorm(h2) * g_attn)
+  a = PostArgsK{};
+  a.eps = sh.eps;
+  a.skip = p.skip;
+  a.N = sh.qkv_dim;
+  a.K = sh.hidden;
+  a.w0 = p.w_qkv;
+  a.g = p.norm_attn;
+  a.x = p.h_out;
+  a.y = p.qkv;
+  return launch_k(gemv_norm_kernel<B>, a.N, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_post_attention(const PostShape &sh, const PostPtrs &p,
+                                 hipStream_t s) {
+  switch (sh.batch) {
+    case 1: return post_b<1>(sh, p, s);
+    case 2: return post_b<2>(sh, p, s);
+    case 3: return post_b<3>(sh, p, s);
+    case 4: return post_b<4>(sh, p, s);
+    case 5: return post_b<5>(sh, p, s);
+    case 6: return post_b<6>(sh, p, s);
+    case 7: return post_b<7>(sh, p, s);
+    case 8: return post_b<8>(sh, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace alspec

@@ -314,6 +314,75 @@ alspec_status alspec_spec_decode_layers(alspec_handle *h,
  * or `stream` is not capturing while it is. */
 alspec_status alspec_order_after_verify(alspec_handle *h, void *stream);
 
+/* ---------------------------------------------------------------------
+ * Post-attention operators of one decoder layer ("Attention-Level
+ * Speculation", research-map page, summary and Approach: the work that the
+ * method runs speculatively on the approximate attention output while the
+ * exact attention is computed, and runs again on the exact output after a
+ * discard).  They follow the Llama decoder layer of the pages' 8B and 70B
+ * shapes, with weights the caller supplies (random here):
+ *   h_out = h1 + W_down (silu(W_gate x) * (W_up x)),
+ *           h1 = h_in + W_o o,  x = rmsnorm(h1) * norm_mlp
+ *   qkv   = W_qkv (rmsnorm(h_out) * norm_attn)
+ * with rmsnorm(v) = v / sqrt(mean(v^2) + eps), per batch entry.  Rotary
+ * position embedding and the new token's K/V append are not applied: the
+ * caller owns the cache (the attention calls take K/V that already hold
+ * the current token).
+ */
+#define ALSPEC_POST_MAX_BATCH 8
+
+typedef struct {
+  int32_t batch;    /* B, 1 .. ALSPEC_POST_MAX_BATCH */
+  int32_t attn_dim; /* width of the attention output (Hq * D), multiple of 8 */
+  int32_t hidden;   /* model width, multiple of 8 */
+  int32_t ffn;      /* MLP width, multiple of 8 */
+  int32_t qkv_dim;  /* rows of the next layer's QKV projection, >= 1 */
+  float eps;        /* RMSNorm epsilon, > 0 and finite */
+} alspec_post_params;
+
+/* Device pointers to bf16 weights (bit patterns, row-major, 16-byte
+ * aligned); none may be NULL. */
+typedef struct {
+  const void *w_o;       /* [hidden][attn_dim] */
+  const void *norm_mlp;  /* [hidden] */
+  const void *w_gate;    /* [ffn][hidden] */
+  const void *w_up;      /* [ffn][hidden] */
+  const void *w_down;    /* [hidden][ffn] */
+  const void *norm_attn; /* [hidden], the next layer's input norm */
+  const void *w_qkv;     /* [qkv_dim][hidden], the next layer's projection */
+} alspec_post_weights;
+
+/* Workspace bytes of alspec_post_attention (the MLP activations,
+ * B x ffn floats).  Pure host computation; validates the parameters. */
+alspec_status alspec_post_workspace_size(const alspec_post_params *p,
+                                         size_t *bytes);
+
+/* The post-attention operators for B entries, four kernel launches on
+ * `stream`, in fp32 arithmetic on bf16 weights.
+ *   o      fp32 [B][attn_dim] attention output (device)
+ *   h_in   fp32 [B][hidden] residual stream in (device)
+ *   h_out  fp32 [B][hidden] residual stream out (device; may equal h_in)
+ *   qkv    fp32 [B][qkv_dim] next layer's projection (device)
+ *   skip   uint8 [B] (device) or NULL: entries whose flag is nonzero are
+ *          left untouched (h_out and qkv not written) -- with the commit
+ *          flags of alspec_spec_decode this replays the operators on the
+ *          exact output only where the speculation was discarded; the
+ *          kernels read the flags on the device and end at once when every
+ *          entry is skipped, so such a call can sit in a captured graph.
+ *   ws     workspace of alspec_post_workspace_size bytes, 256-byte aligned
+ * The caller owns every buffer; nothing is allocated or synchronised.
+ * Pointers must be 16-byte aligned (ALSPEC_ERR_INVALID_ARG otherwise).
+ * Results are deterministic: each output is summed in a fixed order.
+ * h_out must not overlap o or qkv; with skip flags, h_out must not be
+ * h_in (a skipped entry keeps its previous h_out). */
+alspec_status alspec_post_attention(alspec_handle *h,
+                                    const alspec_post_params *p,
+                                    const alspec_post_weights *w,
+                                    const float *o, const float *h_in,
+                                    float *h_out, float *qkv,
+                                    const uint8_t *skip, void *ws,
+                                    size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

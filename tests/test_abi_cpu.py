@@ -214,3 +214,46 @@ def test_layers_chain_validation_before_gpu_work():
     arr[1].ws_bytes = size
     arr[2].q = base + 4                   # misaligned input
     assert f(fake_h, ctypes.byref(p), 4, arr, None) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(batch=9), 2), (dict(attn_dim=12), 1),
+    (dict(hidden=4), 1), (dict(ffn=1001), 1), (dict(qkv_dim=0), 1),
+    (dict(eps=0.0), 1), (dict(eps=float("nan")), 1),
+    (dict(eps=float("inf")), 1)])
+def test_post_workspace_size_validates(kw, status):
+    args = dict(batch=1, attn_dim=64, hidden=64, ffn=128, qkv_dim=32,
+                eps=1e-5)
+    args.update(kw)
+    with pytest.raises(al.AlspecError) as e:
+        al.post_workspace_size(al.make_post_params(**args))
+    assert e.value.status == status
+
+
+def test_post_attention_rejects_before_gpu_work():
+    """Null or misaligned pointers, aliasing outputs, skip flags with an
+    in-place residual and a short workspace are refused before any HIP
+    call (no GPU needed)."""
+    p = al.make_post_params(2, 64, 64, 128, 32)
+    need = al.post_workspace_size(p)
+    assert need == 2 * 128 * 4 + (-(2 * 128 * 4)) % 256
+    f = _binding._post_attention
+    fake_h = ctypes.c_void_p(0x1000)
+    base = 1 << 40
+    w = _binding.PostWeights(*[base + (i << 24) for i in range(7)])
+    o, hi, ho, q, sk, ws = (base + (i << 28) for i in range(8, 14))
+    ok = (o, hi, ho, q, sk, ws, need, None)
+    assert f(None, ctypes.byref(p), ctypes.byref(w), *ok) == 1
+    assert f(fake_h, ctypes.byref(p), None, *ok) == 1
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w),
+             o + 4, hi, ho, q, sk, ws, need, None) == 1       # misaligned
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w),
+             o, hi, hi, q, sk, ws, need, None) == 1           # skip + in place
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w),
+             o, hi, q, q, None, ws, need, None) == 1          # h_out is qkv
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w),
+             o, hi, ho, q, sk, ws, need - 1, None) == 3       # short ws
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w),
+             o, hi, ho, q, sk, ws + 16, need, None) == 3      # misaligned ws
+    w.w_up = None
+    assert f(fake_h, ctypes.byref(p), ctypes.byref(w), *ok) == 1
