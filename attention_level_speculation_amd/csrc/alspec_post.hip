@@ -14,11 +14,12 @@
 // Every product is a skinny matrix-vector product (B <= 8 rows of
 // activations against a bf16 weight matrix read once), so each kernel is
 // bound by HBM bandwidth: 2 bytes per weight for B fused multiply-adds.
-// One wave owns kRows consecutive weight rows and walks the shared
-// dimension K in 16-byte chunks (8 bf16), lane l taking chunks l, l + 64,
-// ...; U chunks per row are loaded before any is used, so about 16 KiB per
-// wave is in flight.  The activations are read from L2 (they are a few KiB
-// and shared by every wave).  The row sums are reduced across the wave by
+// One wave owns kRows (4, 2 or 1, chosen per matrix so that the blocks
+// fill whole rounds of the CUs) consecutive weight rows and walks the
+// shared dimension K in 16-byte chunks (8 bf16), lane l taking chunks l,
+// l + 64, ...; U chunks per row are loaded before any is used.  The
+// activations are read from L2 (they are a few KiB and shared by every
+// wave), for small batches in the same round as the weights.  The row sums are reduced across the wave by
 // butterflies in a fixed order, so results do not depend on timing.
 //
 // The RMSNorm is folded into the products: sum_k W[n][k] (v[k] r g[k]) =
@@ -29,7 +30,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <tuple>
 
 #include "alspec_kernels.h"
 
@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRows = 4;  // weight rows per wave
+constexpr int kCUs = 256;  // compute units of an MI355X
 
 __device__ __forceinline__ void unpack_bf16(const uint4 r, float *f) {
   // A bf16 is the high half of the float32 with the same value.
@@ -81,7 +81,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // (rows past `nrows` repeat the last valid row and are not written by the
 // callers).  With G, ss[b] = sum_k x[b][k]^2.  Sums are complete in every
 // lane on return.
-template <int B, int NW, bool G>
+template <int B, int NW, bool G, int kRows>
 __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
                                           int nrows, int K,
                                           const float *__restrict__ x,
@@ -106,8 +106,13 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
     for (int r = 0; r < kRows; ++r)
       rowp[m][r] = W[m] + (size_t)(n0 + min(r, nrows - 1)) * K;
 
+  // The activation chunks (and norm weights) of small batches are loaded
+  // with the weight chunks, so one wait covers both round trips.
+  constexpr bool XPRE = B <= 2;
   for (int c0 = 0; c0 < nchunk; c0 += 64 * U) {
     uint4 wv[NW][kRows][U];
+    float4 xp[XPRE ? B : 1][U][2];
+    uint4 gp[G && XPRE ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u * 64 + lane, nchunk - 1);
@@ -116,13 +121,26 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
           wv[m][r][u] = *(const uint4 *)(rowp[m][r] + (size_t)c * 8);
+      if constexpr (XPRE) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          xp[b][u][0] = *(const float4 *)(x + (size_t)b * K + c * 8);
+          xp[b][u][1] = *(const float4 *)(x + (size_t)b * K + c * 8 + 4);
+        }
+        if constexpr (G) gp[u] = *(const uint4 *)(g + (size_t)c * 8);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 64 + lane;
       if (c < nchunk) {
         float gs[8];
-        if constexpr (G) unpack_bf16(*(const uint4 *)(g + (size_t)c * 8), gs);
+        if constexpr (G) {
+          if constexpr (XPRE)
+            unpack_bf16(gp[u], gs);
+          else
+            unpack_bf16(*(const uint4 *)(g + (size_t)c * 8), gs);
+        }
         float wf[NW][kRows][8];
 #pragma unroll
         for (int m = 0; m < NW; ++m)
@@ -130,8 +148,14 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
           for (int r = 0; r < kRows; ++r) unpack_bf16(wv[m][r][u], wf[m][r]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          const float4 xa = *(const float4 *)(x + (size_t)b * K + c * 8);
-          const float4 xb = *(const float4 *)(x + (size_t)b * K + c * 8 + 4);
+          float4 xa, xb;
+          if constexpr (XPRE) {
+            xa = xp[b][u][0];
+            xb = xp[b][u][1];
+          } else {
+            xa = *(const float4 *)(x + (size_t)b * K + c * 8);
+            xb = *(const float4 *)(x + (size_t)b * K + c * 8 + 4);
+          }
           float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
           if constexpr (G) {
 #pragma unroll
@@ -175,7 +199,7 @@ struct PostArgsK {
 
 // y[b][n] = base[b][n] + sum_k W[n][k] x[b][k]   (output and down
 // projections; y may alias base).
-template <int B>
+template <int B, int kRows>
 __global__ __launch_bounds__(kThreads) void gemv_residual_kernel(PostArgsK a) {
   if (!any_active<B>(a.skip)) return;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -184,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void gemv_residual_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[1] = {a.w0};
   float acc[1][kRows][B], ss[B];
-  wave_rows<B, 1, false>(W, n0, nrows, a.K, a.x, nullptr, acc, ss);
+  wave_rows<B, 1, false, kRows>(W, n0, nrows, a.K, a.x, nullptr, acc, ss);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -203,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void gemv_residual_kernel(PostArgsK a) {
 
 // m[b][n] = silu(r_b gate) * (r_b up), gate/up = sum_k W_{gate,up}[n][k]
 // x[b][k] g[k], r_b = 1 / sqrt(mean_k x[b][k]^2 + eps).
-template <int B>
+template <int B, int kRows>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(PostArgsK a) {
   if (!any_active<B>(a.skip)) return;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[2] = {a.w0, a.w1};
   float acc[2][kRows][B], ss[B];
-  wave_rows<B, 2, true>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  wave_rows<B, 2, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -238,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(PostArgsK a) {
 }
 
 // y[b][n] = r_b sum_k W[n][k] x[b][k] g[k]   (next layer's QKV).
-template <int B>
+template <int B, int kRows>
 __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
   if (!any_active<B>(a.skip)) return;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -247,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[1] = {a.w0};
   float acc[1][kRows][B], ss[B];
-  wave_rows<B, 1, true>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  wave_rows<B, 1, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -265,19 +289,49 @@ __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
   }
 }
 
-template <typename... KArgs, typename... Args>
-hipError_t launch_k(void (*kern)(KArgs...), int n_rows, hipStream_t s,
-                    Args &&...args) {
-  const int waves = (n_rows + kRows - 1) / kRows;
-  const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
-  std::tuple<KArgs...> t(std::forward<Args>(args)...);
-  void *argv[sizeof...(KArgs)];
-  std::apply([&](auto &...e) {
-    int i = 0;
-    ((argv[i++] = (void *)&e), ...);
-  }, t);
-  return hipLaunchKernel((const void *)kern, grid, block, argv, 0, s);
+// Rows per wave for N rows: of 2, 4 and 1 (in that order of preference:
+// two rows per wave measured fastest where all fill the CUs evenly), the
+// one whose blocks (4 waves each) fill whole rounds of the 256 CUs best, so
+// no CU runs an extra block while others idle.
+int rows_per_wave(int N) {
+  int best = 2;
+  double best_eff = -1.0;
+  for (int r : {2, 4, 1}) {
+    const long blocks = ((N + r - 1) / r + kWaves - 1) / kWaves;
+    const long rounds = (blocks + kCUs - 1) / kCUs;
+    const double eff = (double)blocks / (double)(rounds * kCUs);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = r;
+    }
+  }
+  return best;
 }
+
+template <template <int, int> class K, int B>
+hipError_t launch_k(int n_rows, hipStream_t s, PostArgsK a) {
+  const int r = rows_per_wave(n_rows);
+  const int waves = (n_rows + r - 1) / r;
+  const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
+  void *argv[1] = {&a};
+  const void *kern = r == 4   ? K<B, 4>::ptr()
+                     : r == 2 ? K<B, 2>::ptr()
+                              : K<B, 1>::ptr();
+  return hipLaunchKernel(kern, grid, block, argv, 0, s);
+}
+
+template <int B, int R>
+struct ResidualK {
+  static const void *ptr() { return (const void *)gemv_residual_kernel<B, R>; }
+};
+template <int B, int R>
+struct GateUpK {
+  static const void *ptr() { return (const void *)gate_up_kernel<B, R>; }
+};
+template <int B, int R>
+struct NormK {
+  static const void *ptr() { return (const void *)gemv_norm_kernel<B, R>; }
+};
 
 template <int B>
 hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
@@ -291,7 +345,7 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.x = p.o;
   a.base = p.h_in;
   a.y = p.h_out;
-  hipError_t e = launch_k(gemv_residual_kernel<B>, a.N, s, a);
+  hipError_t e = launch_k<ResidualK, B>(a.N, s, a);
   if (e != hipSuccess) return e;
   // m = silu(gate) * up over rmsnorm(h1) * g_mlp
   a = PostArgsK{};
@@ -304,7 +358,7 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.g = p.norm_mlp;
   a.x = p.h_out;
   a.y = p.m;
-  e = launch_k(gate_up_kernel<B>, a.N, s, a);
+  e = launch_k<GateUpK, B>(a.N, s, a);
   if (e != hipSuccess) return e;
   // h2 = h1 + W_down m, in place
   a = PostArgsK{};
@@ -316,7 +370,7 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.x = p.m;
   a.base = p.h_out;
   a.y = p.h_out;
-  e = launch_k(gemv_residual_kernel<B>, a.N, s, a);
+  e = launch_k<ResidualK, B>(a.N, s, a);
   if (e != hipSuccess) return e;
   // qkv = W_qkv (rmsnorm(h2) * g_attn)
   a = PostArgsK{};
@@ -328,7 +382,7 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.g = p.norm_attn;
   a.x = p.h_out;
   a.y = p.qkv;
-  return launch_k(gemv_norm_kernel<B>, a.N, s, a);
+  return launch_k<NormK, B>(a.N, s, a);
 }
 
 }  // namespace
