@@ -129,6 +129,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--model-steps", type=int, default=10,
+                    help="timed tokens of the chained decode step with "
+                         "post-attention work (0: skip)")
     return ap.parse_args()
 
 
@@ -554,6 +557,13 @@ def main():
             out["roofline"] = exact_pass
         out["roofline"]["approx_tokens_per_head"] = a_tokens
 
+    # ---- chained decode step with post-attention work -------------------
+    if args.model_steps > 0:
+        di4 = dens.index(4) if 4 in dens else 0
+        out["model_step"] = model_timing(args, al, h, works[di4], Qs[di4],
+                                         Ks[di4], Vs[di4], nl, dev)
+        log("model step done")
+
     # ---- CPU oracle baseline --------------------------------------------
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, works, dens, outs, nl, Qs,
@@ -576,6 +586,116 @@ def main():
 
     print(json.dumps(out), flush=True)
     h.close()
+
+
+def model_timing(args, al, h, w, Q, K, V, nl, dev):
+    """One decode token through nl Llama-3-8B-shaped layers: the attention
+    step on the resident 128K KV, then the post-attention operators with
+    seeded random bf16 weights (o_proj, RMSNorm + gated MLP, down, RMSNorm
+    + next QKV; 416 MiB per layer), layer l+1's query from layer l's QKV.
+    Timed eagerly (the two-stream step cannot be captured, see the runtime
+    module), by wall clock between synchronisations, in three forms:
+      exact_only      exact attention, then post-attention on its output
+      spec_sequence   attention step with verify, then post-attention on
+                      the committed output, one stream
+      spec_overlap    the same result with the post-attention work run on
+                      o_approx beside the exact pass and replayed on o_exact
+                      after a discard (runtime.model_step)
+    The last at lambda 0.10 and, to bracket it, at +inf (every layer
+    commits) and 0 (every layer discards).  Also the post-attention kernels
+    alone against the HBM roofline (HIP events around back-to-back layers).
+    """
+    import torch
+
+    from attention_level_speculation_amd import runtime as rt
+    from synth import post_gen as pg
+    ps = pg.llama8b(B=1)
+    pp = al.make_post_params(1, ps.attn_dim, ps.hidden, ps.ffn, ps.qkv_dim,
+                             ps.eps)
+    gen_ = torch.Generator(device=dev)
+    gen_.manual_seed(ps.seed)
+    weights = []
+    for layer in range(nl):
+        d = {}
+        for n_, shp in ps.shapes().items():
+            if n_.startswith("norm"):
+                t = 1.0 + 0.1 * torch.randn(shp, device=dev, generator=gen_)
+            else:
+                t = torch.randn(shp, device=dev, generator=gen_)
+                t *= shp[1] ** -0.5
+            d[n_] = t.to(torch.bfloat16)
+        weights.append(d)
+    structs = [al.post_weights_struct(pp, d) for d in weights]
+    f = dict(dtype=torch.float32, device=dev)
+    hs = [torch.randn((1, ps.hidden), generator=gen_, **f)] + [
+        torch.empty((1, ps.hidden), **f) for _ in range(nl)]
+    qkvs = [torch.empty((1, ps.qkv_dim), **f) for _ in range(nl)]
+    wsp = (al.alloc_post_workspace(pp, dev), al.alloc_post_workspace(pp, dev))
+    sa, se = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    cur = torch.cuda.current_stream()
+    res = {"workload": "llama3-8b-shaped decoder layers, batch 1: attention "
+                       "over the 128K bf16 KV of one density (4 needles), "
+                       "then post-attention with seeded random bf16 "
+                       "weights", "layers": nl,
+           "post_weight_bytes_per_layer": ps.weight_bytes(),
+           "steps": args.model_steps}
+
+    # post-attention kernels alone
+    o_ = torch.randn((1, ps.attn_dim), generator=gen_, **f)
+    for i in range(8):
+        al.post_attention(h, pp, structs[i % nl], o_, hs[0], hs[1], qkvs[0],
+                          wsp[1], stream=se)
+    torch.cuda.synchronize()
+    reps = max(1, args.kernel_launches // 4)
+    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0.record(se)
+    for i in range(reps):
+        al.post_attention(h, pp, structs[i % nl], o_, hs[0], hs[1], qkvs[0],
+                          wsp[1], stream=se)
+    e1.record(se)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbps = ps.weight_bytes() / (us * 1e-6) / 1e9
+    res["post_attention_roofline"] = {
+        "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+        "kernels": "gemv_residual (o_proj), gate_up, gemv_residual (down), "
+                   "gemv_norm (next QKV), one layer",
+        "algorithmic_bytes_per_layer": ps.weight_bytes(),
+        "us_per_layer": us, "layers_timed": reps}
+
+    def run(lam, **kw):
+        p = al.params_for(w, lam=lam)
+        outs = [al.alloc_outputs(p, dev) for _ in range(nl)]
+        layers = [rt.ModelLayer(K[l], V[l], structs[l], outs[l], hs[l],
+                                hs[l + 1], qkvs[l]) for l in range(nl)]
+        ws = al.alloc_workspace(p, dev)
+
+        def step():
+            sa.wait_stream(cur)
+            se.wait_stream(cur)
+            rt.model_step(h, p, pp, Q[0], layers, ws, wsp[0], wsp[1], sa, se,
+                          **kw)
+            cur.wait_stream(sa)
+            cur.wait_stream(se)
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.model_steps):
+            step()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.model_steps
+        commits = [int(o["commit"][0].item()) for o in outs]
+        return {"us_per_layer": wall * 1e6 / nl,
+                "tokens_layers_per_s": nl / wall,
+                "commit_rate": sum(commits) / nl}
+    res["exact_only"] = run(w.lam, exact_only=True)
+    res["exact_only"].pop("commit_rate")
+    res["spec_sequence"] = run(w.lam, speculative=False)
+    res["spec_overlap"] = run(w.lam, speculative=True)
+    res["spec_overlap_all_commit"] = run(float("inf"), speculative=True)
+    res["spec_overlap_all_discard"] = run(0.0, speculative=True)
+    return res
 
 
 def kernel_timing(args, al, B_, h, p, Qs, Ks, Vs, stream, nd, nl):
