@@ -563,6 +563,13 @@ def main():
         out["model_step"] = model_timing(args, al, h, works[di4], Qs[di4],
                                          Ks[di4], Vs[di4], nl, dev)
         log("model step done")
+        seq = res.get("sequential", {})
+        if ("approx_latency_us_mean" in seq and
+                "exact_only_baseline" in res):
+            out["projection"] = projection(
+                seq, res["exact_only_baseline"]["ms_per_step"] * 1e3 / nl,
+                out["model_step"]["post_attention_roofline"]["us_per_layer"],
+                hit_rate)
 
     # ---- CPU oracle baseline --------------------------------------------
     if not args.no_cpu_baseline:
@@ -586,6 +593,57 @@ def main():
 
     print(json.dumps(out), flush=True)
     h.close()
+
+
+# Assumed xGMI figures for the projection (no second GPU here): latency of
+# a small point-to-point transfer (a commit flag or an 8-16 KiB output) and
+# of a small all-reduce across the GPUs of a tensor-parallel group.
+XGMI_P2P_US = 5.0
+XGMI_ALLREDUCE_US = 10.0
+
+
+def projection(seq, exact_only_us, post_us, hit):
+    """Per-layer latency of one decode token projected from this run's
+    MI355X kernel durations to placements on two GPUs, as the pages
+    projected H100 from measured durations ([A] Key results, Limitations):
+    host and dispatch latency excluded, link figures assumed.
+      one_gpu          exact attention, then post-attention, in turn
+      alspec_2gpu      the pages' placement: GPU A runs exact attention and
+                       the verify; GPU B runs the approximation and the
+                       post-attention work on it and goes on to the next
+                       layer.  Commit: the two run side by side, so a layer
+                       costs max(approx + post, exact to verified output +
+                       link).  Discard: B waits for the exact output, then
+                       replays the post-attention work.
+      tp_2gpu          tensor parallel over two GPUs, no speculation:
+                       attention and post-attention each halved, plus the
+                       two all-reduces of a decoder layer (after the output
+                       projection and after the MLP)."""
+    t_a = seq["approx_latency_us_mean"]
+    t_e = seq["exact_latency_us_mean"]
+    one = exact_only_us + post_us
+    commit = max(t_a + post_us, t_e + XGMI_P2P_US)
+    discard = t_e + XGMI_P2P_US + post_us
+    alspec = hit * commit + (1.0 - hit) * discard
+    tp2 = (exact_only_us + post_us) / 2.0 + 2 * XGMI_ALLREDUCE_US
+    return {
+        "inputs_us": {"approximation": t_a,
+                      "exact_to_verified_output": t_e,
+                      "exact_only_attention": exact_only_us,
+                      "post_attention": post_us,
+                      "assumed_xgmi_p2p": XGMI_P2P_US,
+                      "assumed_xgmi_allreduce": XGMI_ALLREDUCE_US},
+        "hit_rate": hit,
+        "us_per_layer": {"one_gpu": one, "alspec_2gpu_commit": commit,
+                         "alspec_2gpu_discard": discard,
+                         "alspec_2gpu": alspec, "tp_2gpu": tp2},
+        "speedup_vs_one_gpu": {"alspec_2gpu": one / alspec,
+                               "tp_2gpu": one / tp2},
+        "note": "a model, not a measurement: durations measured on one "
+                "MI355X, the link figures assumed; the post-attention "
+                "weights are random, the hit rate is this run's attention "
+                "hit rate on the synthetic inputs",
+    }
 
 
 def model_timing(args, al, h, w, Q, K, V, nl, dev):
