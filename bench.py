@@ -83,12 +83,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "02a70ff9742afc5a027d30298abf5deb"
-                     "778688b9187e943c3d6ebd9ba79391bc",
+           "sha256": "d458fdc600c5dc29877a6335dc4698fd"
+                     "6637442137857156cecbd75be45946e5",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262902.0 * 1024 * 2.0, 871.3 * 1024 * 1.0),
-                     "partials_middle": (258200.0 * 1024 * 2.0,
+           "bytes": {"chain": (262902.9 * 1024 * 2.0, 871.3 * 1024 * 1.0),
+                     "partials_middle": (258199.3 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
