@@ -289,14 +289,17 @@ __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
   }
 }
 
-// Rows per wave for N rows: of 2, 4 and 1 (in that order of preference:
-// two rows per wave measured fastest where all fill the CUs evenly), the
-// one whose blocks (4 waves each) fill whole rounds of the 256 CUs best, so
-// no CU runs an extra block while others idle.
-int rows_per_wave(int N) {
-  int best = 2;
+// Rows per wave for N rows: of 2, 4 and 1 (two rows first for one or two
+// entries, four first for more, as measured fastest where all fill the CUs
+// evenly), the one whose blocks (4 waves each) fill whole rounds of the
+// 256 CUs best, so no CU runs an extra block while others idle.
+int rows_per_wave(int N, int B) {
+  const int order_small[3] = {2, 4, 1}, order_large[3] = {4, 2, 1};
+  const int *order = B <= 2 ? order_small : order_large;
+  int best = order[0];
   double best_eff = -1.0;
-  for (int r : {2, 4, 1}) {
+  for (int i = 0; i < 3; ++i) {
+    const int r = order[i];
     const long blocks = ((N + r - 1) / r + kWaves - 1) / kWaves;
     const long rounds = (blocks + kCUs - 1) / kCUs;
     const double eff = (double)blocks / (double)(rounds * kCUs);
@@ -310,7 +313,7 @@ int rows_per_wave(int N) {
 
 template <template <int, int> class K, int B>
 hipError_t launch_k(int n_rows, hipStream_t s, PostArgsK a) {
-  const int r = rows_per_wave(n_rows);
+  const int r = rows_per_wave(n_rows, B);
   const int waves = (n_rows + r - 1) / r;
   const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
   void *argv[1] = {&a};
