@@ -304,6 +304,34 @@ __device__ __forceinline__ void split3(const float *x, bf16x8 &hi,
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// Butterfly steps across 16- and 32-lane rows on the VALU (gfx950 row
+// swaps): lane l gets op(x[l], x[l ^ 16]) or op(x[l], x[l ^ 32]).  Swapping
+// a register with itself leaves rows (0, 0, 2, 2) in one result and
+// (1, 1, 3, 3) in the other (for 32: low half twice, high half twice), so
+// the two results hold each lane's pair.  Sum and max are commutative, so
+// the bits equal those of the same step done with a shuffle.  All 64 lanes
+// must be active.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -324,17 +352,19 @@ struct MfmaWave {
   static constexpr int D = 128;
   static constexpr int TILE = 16;
   static constexpr int STEP = kWaves * TILE;
+  static_assert(kWaves == 4, "one wave per 32-wide slice of q");
   int lane, wave, r, c;
   float m_lane;  // running max of head r (same in all 4 rows)
   float l_lane;  // this lane's share of head r's normaliser
   float acc[G][8];
 
+  // Lane indices only: the softmax state is set by reset() or by the first
+  // tile (tile<true>), whichever comes first.
   __device__ __forceinline__ void init() {
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     r = lane & 15;
     c = lane >> 4;
-    reset();
   }
   __device__ __forceinline__ void reset() {
     m_lane = neg_inf();
@@ -364,35 +394,38 @@ struct MfmaWave {
     }
   }
 
-  // q of head r into the shared operands (wave 0; columns r >= G are
-  // padding: a valid row is read and zeroed, so the loads need no branch
-  // and go out together).  The caller synchronises the block.
-  __device__ __forceinline__ void prepare_q(const float *__restrict__ qg,
-                                            float sm_log2,
-                                            MfmaShared<G> &sh) const {
-    if (wave != 0) return;
+  // q of head r, D slice s = wave (each of the four waves takes one 32-wide
+  // slice; columns r >= G are padding: a valid row is read, and zeroed in
+  // prepare_q, so the loads need no branch and go out together).
+  __device__ __forceinline__ void load_q(const float *__restrict__ qg,
+                                         float4 (&qv)[2]) const {
     const float4 *qr =
         (const float4 *)(qg + (size_t)(r < G ? r : G - 1) * D + 32 * c);
+    qv[0] = qr[2 * wave];
+    qv[1] = qr[2 * wave + 1];
+  }
+
+  // This wave's slice of q, scaled and split, into the shared operands.
+  // The caller synchronises the block.
+  __device__ __forceinline__ void prepare_q(const float4 (&qv)[2],
+                                            float sm_log2,
+                                            MfmaShared<G> &sh) const {
     const float qs = r < G ? sm_log2 : 0.f;
-    float4 qv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = qr[i];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float x[8] = {qv[2 * s].x * qs,     qv[2 * s].y * qs,
-                          qv[2 * s].z * qs,     qv[2 * s].w * qs,
-                          qv[2 * s + 1].x * qs, qv[2 * s + 1].y * qs,
-                          qv[2 * s + 1].z * qs, qv[2 * s + 1].w * qs};
-      bf16x8 qh, qm, ql;
-      split3(x, qh, qm, ql);
-      sh.q[0][s][lane] = qh;
-      sh.q[1][s][lane] = qm;
-      sh.q[2][s][lane] = ql;
-    }
+    const float x[8] = {qv[0].x * qs, qv[0].y * qs, qv[0].z * qs,
+                        qv[0].w * qs, qv[1].x * qs, qv[1].y * qs,
+                        qv[1].z * qs, qv[1].w * qs};
+    bf16x8 qh, qm, ql;
+    split3(x, qh, qm, ql);
+    sh.q[0][wave][lane] = qh;
+    sh.q[1][wave][lane] = qm;
+    sh.q[2][wave][lane] = ql;
   }
 
   // One 16-token tile of this wave (rows from tb, range end t1): logits on
-  // MFMA, online softmax, P*V.
+  // MFMA, online softmax, P*V.  FIRST: the wave's first tile, which sets
+  // the state instead of updating it (the same bits as an update of the
+  // reset state, whose scale factor is 0, up to the sign of a zero).
+  template <bool FIRST = false>
   __device__ __forceinline__ void tile(int tb, int t1, const u32x4 (&kr)[4],
                                        const u32x4 (&vr)[4],
                                        MfmaShared<G> &sh) {
@@ -415,13 +448,15 @@ struct MfmaWave {
       sv[j] = (tb + 4 * c + j < t1) ? a4[j] : neg_inf();
       mx = fmaxf(mx, sv[j]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_lane, mx);
+    mx = xor32_max(xor16_max(mx));
+    const float mnew = FIRST ? mx : fmaxf(m_lane, mx);
     const float ref = exp_ref(mnew);
-    const float sc = fast_exp2(m_lane - ref);
+    float ls = 0.f, sc = 0.f;
+    if constexpr (!FIRST) {
+      sc = fast_exp2(m_lane - ref);
+      ls = l_lane * sc;
+    }
     m_lane = mnew;
-    float ls = l_lane * sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float pj = fast_exp2(sv[j] - ref);
@@ -430,11 +465,13 @@ struct MfmaWave {
     }
     l_lane = ls;
     // rescale: head h's factor is uniform, held by lane h
+    if constexpr (!FIRST) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float shh = readlane_f(sc, h);
+      for (int h = 0; h < G; ++h) {
+        const float shh = readlane_f(sc, h);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] *= shh;
+        for (int i = 0; i < 8; ++i) acc[h][i] *= shh;
+      }
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -453,7 +490,9 @@ struct MfmaWave {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
+        for (int i = 0; i < 8; ++i)
+          acc[h][i] = (FIRST && j == 0) ? pv[h] * vf[i]
+                                        : acc[h][i] + pv[h] * vf[i];
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -465,15 +504,11 @@ struct MfmaWave {
   __device__ __forceinline__ void finish(MfmaShared<G> &sh,
                                          float2 *__restrict__ out_ml,
                                          float *__restrict__ out_acc) {
-    l_lane += __shfl_xor(l_lane, 16);
-    l_lane += __shfl_xor(l_lane, 32);
+    l_lane = xor32_sum(xor16_sum(l_lane));
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[h][i] += __shfl_xor(acc[h][i], 16);
-        acc[h][i] += __shfl_xor(acc[h][i], 32);
-      }
+      for (int i = 0; i < 8; ++i) acc[h][i] = xor32_sum(xor16_sum(acc[h][i]));
     if (c == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -537,18 +572,34 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
   const int last = t1 - 1;
   const int ta0 = t0 + wv.wave * TILE;  // this wave's tile i is at ta0 + i*STEP
 
-  // The first tiles' loads go out before q is read and split, so the round
-  // trips overlap.  Rows past the range are clamped to its last row.
+  // Each wave's q slice is requested first, so its wait for q leaves the
+  // tiles in flight.  With G = 4, a split of at most two steps (the sink
+  // and window splits of windows up to 2048 tokens) requests both its
+  // tiles at once and runs without a loop; a longer one starts NS - 1 tiles
+  // ahead and requests each next tile in its loop (preloading one more
+  // costs 25 VGPRs there).  At G = 8 the short form would cost occupancy
+  // (176 VGPRs), and the plans give G = 8 windows of 4096 tokens, whose
+  // splits take four steps anyway.  Rows past the range are clamped to its
+  // last row.
+  constexpr bool kShortPath = G == 4;
   u32x4 kr[NS][4], vr[NS][4];
-  if (t0 < t1) {
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
-  }
-  wv.prepare_q(qg, sm_log2, sh);
-  __syncthreads();
-
-  if constexpr (NS == 2) {
+  float4 qv[2];
+  wv.load_q(qg, qv);
+  if (kShortPath && t1 - t0 <= 2 * STEP) {
+    if (t0 < t1) wv.load(kb, vb, ta0, last, kr[0], vr[0]);
+    if (t0 + STEP < t1) wv.load(kb, vb, ta0 + STEP, last, kr[1], vr[1]);
+    wv.prepare_q(qv, sm_log2, sh);
+    __syncthreads();
+    if (t0 < t1)
+      wv.template tile<true>(ta0, t1, kr[0], vr[0], sh);
+    else
+      wv.reset();
+    if (t0 + STEP < t1) wv.tile(ta0 + STEP, t1, kr[1], vr[1], sh);
+  } else if constexpr (NS == 2) {
+    wv.reset();
+    wv.load(kb, vb, ta0, last, kr[0], vr[0]);
+    wv.prepare_q(qv, sm_log2, sh);
+    __syncthreads();
     // spelled out: the compiler keeps this form in 18 fewer VGPRs
     for (int blk = t0; blk < t1; blk += 2 * STEP) {
       const int ta = blk + wv.wave * TILE;
@@ -559,6 +610,12 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
       wv.tile(ta + STEP, t1, kr[1], vr[1], sh);
     }
   } else {
+    wv.reset();
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
+    wv.prepare_q(qv, sm_log2, sh);
+    __syncthreads();
     for (int blk = t0; blk < t1; blk += NS * STEP) {
       const int ta = blk + wv.wave * TILE;
 #pragma unroll
@@ -797,8 +854,11 @@ __device__ __forceinline__ Item decode_item(const PlanArgs &pa,
 }
 
 // Slots merged per thread per memory round in the merges of the sink and
-// window states (a handful of splits).
-constexpr int kMergeRoundA = 8;
+// window states.  The plan gives 16 window splits plus one sink split
+// for windows of 1024 to 8192 tokens, and the merge's two slot
+// groups per head then take all 17 in one round (at 8 a second round and a
+// separate max pass would each add a dependent round trip).
+constexpr int kMergeRoundA = 9;
 // ... and in the exact merges (many middle splits).
 constexpr int kMergeRoundM = 8;
 
