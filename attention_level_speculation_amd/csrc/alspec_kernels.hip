@@ -81,6 +81,34 @@ struct KvBf16 {
 
 // ------------------------------------------------------- lane reductions ---
 
+// Butterfly steps across 16- and 32-lane rows on the VALU (gfx950 row
+// swaps): lane l gets op(x[l], x[l ^ 16]) or op(x[l], x[l ^ 32]).  Swapping
+// a register with itself leaves rows (0, 0, 2, 2) in one result and
+// (1, 1, 3, 3) in the other (for 32: low half twice, high half twice), so
+// the two results hold each lane's pair.  Sum and max are commutative, so
+// the bits equal those of the same step done with a shuffle.  All 64 lanes
+// must be active.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(
@@ -96,15 +124,25 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
   if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
   if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+// Max over aligned groups of N lanes (N a power of two <= 64), in every
+// lane of the group.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_mov<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
+
+__device__ __forceinline__ float wave_max(float x) { return group_max<64>(x); }
 
 // ------------------------------------------------- one split of one head ---
 
@@ -304,34 +342,6 @@ __device__ __forceinline__ void split3(const float *x, bf16x8 &hi,
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Butterfly steps across 16- and 32-lane rows on the VALU (gfx950 row
-// swaps): lane l gets op(x[l], x[l ^ 16]) or op(x[l], x[l ^ 32]).  Swapping
-// a register with itself leaves rows (0, 0, 2, 2) in one result and
-// (1, 1, 3, 3) in the other (for 32: low half twice, high half twice), so
-// the two results hold each lane's pair.  Sum and max are commutative, so
-// the bits equal those of the same step done with a shuffle.  All 64 lanes
-// must be active.
-__device__ __forceinline__ float xor16_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor16_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -358,13 +368,12 @@ struct MfmaWave {
   float l_lane;  // this lane's share of head r's normaliser
   float acc[G][8];
 
-  // Lane indices only: the softmax state is set by reset() or by the first
-  // tile (tile<true>), whichever comes first.
   __device__ __forceinline__ void init() {
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     r = lane & 15;
     c = lane >> 4;
+    reset();
   }
   __device__ __forceinline__ void reset() {
     m_lane = neg_inf();
@@ -422,10 +431,7 @@ struct MfmaWave {
   }
 
   // One 16-token tile of this wave (rows from tb, range end t1): logits on
-  // MFMA, online softmax, P*V.  FIRST: the wave's first tile, which sets
-  // the state instead of updating it (the same bits as an update of the
-  // reset state, whose scale factor is 0, up to the sign of a zero).
-  template <bool FIRST = false>
+  // MFMA, online softmax, P*V.
   __device__ __forceinline__ void tile(int tb, int t1, const u32x4 (&kr)[4],
                                        const u32x4 (&vr)[4],
                                        MfmaShared<G> &sh) {
@@ -449,14 +455,11 @@ struct MfmaWave {
       mx = fmaxf(mx, sv[j]);
     }
     mx = xor32_max(xor16_max(mx));
-    const float mnew = FIRST ? mx : fmaxf(m_lane, mx);
+    const float mnew = fmaxf(m_lane, mx);
     const float ref = exp_ref(mnew);
-    float ls = 0.f, sc = 0.f;
-    if constexpr (!FIRST) {
-      sc = fast_exp2(m_lane - ref);
-      ls = l_lane * sc;
-    }
+    const float sc = fast_exp2(m_lane - ref);
     m_lane = mnew;
+    float ls = l_lane * sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float pj = fast_exp2(sv[j] - ref);
@@ -465,13 +468,11 @@ struct MfmaWave {
     }
     l_lane = ls;
     // rescale: head h's factor is uniform, held by lane h
-    if constexpr (!FIRST) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float shh = readlane_f(sc, h);
+    for (int h = 0; h < G; ++h) {
+      const float shh = readlane_f(sc, h);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= shh;
-      }
+      for (int i = 0; i < 8; ++i) acc[h][i] *= shh;
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -490,9 +491,7 @@ struct MfmaWave {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          acc[h][i] = (FIRST && j == 0) ? pv[h] * vf[i]
-                                        : acc[h][i] + pv[h] * vf[i];
+        for (int i = 0; i < 8; ++i) acc[h][i] += pv[h] * vf[i];
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -572,34 +571,24 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
   const int last = t1 - 1;
   const int ta0 = t0 + wv.wave * TILE;  // this wave's tile i is at ta0 + i*STEP
 
-  // Each wave's q slice is requested first, so its wait for q leaves the
-  // tiles in flight.  With G = 4, a split of at most two steps (the sink
-  // and window splits of windows up to 2048 tokens) requests both its
-  // tiles at once and runs without a loop; a longer one starts NS - 1 tiles
-  // ahead and requests each next tile in its loop (preloading one more
-  // costs 25 VGPRs there).  At G = 8 the short form would cost occupancy
-  // (176 VGPRs), and the plans give G = 8 windows of 4096 tokens, whose
-  // splits take four steps anyway.  Rows past the range are clamped to its
-  // last row.
-  constexpr bool kShortPath = G == 4;
+  // Each wave's q slice is requested first and the first NS - 1 tiles
+  // after it, so each wave's wait for its q slice leaves the tiles in
+  // flight.  Rows past the range are clamped to its last row.  (A loop-free
+  // form for splits of two steps, meant to request both tiles at once,
+  // measured slower: the compiler placed its tile loads behind the wait for
+  // q, and it cost 12 VGPRs.)
   u32x4 kr[NS][4], vr[NS][4];
   float4 qv[2];
   wv.load_q(qg, qv);
-  if (kShortPath && t1 - t0 <= 2 * STEP) {
-    if (t0 < t1) wv.load(kb, vb, ta0, last, kr[0], vr[0]);
-    if (t0 + STEP < t1) wv.load(kb, vb, ta0 + STEP, last, kr[1], vr[1]);
-    wv.prepare_q(qv, sm_log2, sh);
-    __syncthreads();
-    if (t0 < t1)
-      wv.template tile<true>(ta0, t1, kr[0], vr[0], sh);
-    else
-      wv.reset();
-    if (t0 + STEP < t1) wv.tile(ta0 + STEP, t1, kr[1], vr[1], sh);
-  } else if constexpr (NS == 2) {
-    wv.reset();
-    wv.load(kb, vb, ta0, last, kr[0], vr[0]);
-    wv.prepare_q(qv, sm_log2, sh);
-    __syncthreads();
+  if (t0 < t1) {
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
+  }
+  wv.prepare_q(qv, sm_log2, sh);
+  __syncthreads();
+
+  if constexpr (NS == 2) {
     // spelled out: the compiler keeps this form in 18 fewer VGPRs
     for (int blk = t0; blk < t1; blk += 2 * STEP) {
       const int ta = blk + wv.wave * TILE;
@@ -610,12 +599,6 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
       wv.tile(ta + STEP, t1, kr[1], vr[1], sh);
     }
   } else {
-    wv.reset();
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
-    wv.prepare_q(qv, sm_log2, sh);
-    __syncthreads();
     for (int blk = t0; blk < t1; blk += NS * STEP) {
       const int ta = blk + wv.wave * TILE;
 #pragma unroll
@@ -690,9 +673,7 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
     for (int i = u; i < n; i += TPH)
       mx = fmaxf(mx, ml[(size_t)(slot0 + i) * Hq + h].x);
   }
-#pragma unroll
-  for (int off = (TPH < 64 ? TPH : 64) / 2; off >= 1; off >>= 1)
-    mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = group_max<(TPH < 64 ? TPH : 64)>(mx);
   if (TPH >= 64) {
     if ((u & 63) == 0) s_mx[hh][u >> 6] = mx;
   } else if (u == 0) {
@@ -786,6 +767,16 @@ __device__ __forceinline__ float ratio_of(float num, float den) {
   if (isnan(num) || isnan(den)) return __builtin_nanf("");
   if (den > 0.f) return sqrtf(num / den);
   return num == 0.f ? 0.f : __builtin_huge_valf();
+}
+
+// Arrival counters (each on its own line): exact-merge heads of entry b,
+// and sink/window splits of (entry b, kv head g).
+__device__ __forceinline__ unsigned *user_counter(const WsPtrs &w, int b) {
+  return w.counters + kUserCounters + b * kCounterStride;
+}
+__device__ __forceinline__ unsigned *approx_counter(const WsPtrs &w, int b,
+                                                    int Hkv, int g) {
+  return w.counters + kApproxCounters + (b * Hkv + g) * kCounterStride;
 }
 
 // Returns true in every thread of the block for the last block to arrive at
@@ -1090,7 +1081,7 @@ __global__ __launch_bounds__(kThreads) void approx_fused_kernel(
                             w.part_ml + (size_t)it.slot * Hq + h0,
                             w.part_acc + ((size_t)it.slot * Hq + h0) * D);
   const unsigned n = (unsigned)(pa.nsink[it.b] + pa.nwin[it.b]);
-  if (!arrive_last(w.counters + kApproxCounters + it.b * pa.Hkv + it.g, n))
+  if (!arrive_last(approx_counter(w, it.b, pa.Hkv, it.g), n))
     return;
   approx_merge<D, G>(pa, w, o, it.b, it.g);
 }
@@ -1114,7 +1105,7 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
                                                                 Outs o) {
   const int b = blockIdx.x / pa.Hq, h = blockIdx.x % pa.Hq;
   exact_heads<D, 1>(pa, w, b, h, o.o_approx, o.o_exact, o.lse_exact);
-  if (!arrive_last(w.counters + kUserCounters + b, (unsigned)pa.Hq)) return;
+  if (!arrive_last(user_counter(w, b), (unsigned)pa.Hq)) return;
   finalize_entry<D>(pa, w, b, o.o_approx, o.o_exact, o.ratio, o.commit,
                     o.o_committed, o.lambda);
 }
@@ -1150,7 +1141,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
     const int b = idx / Hq, h = idx % Hq;
     exact_heads<D, 1>(pa, ver.w, b, h, ver.o.o_approx, ver.o.o_exact,
                       ver.o.lse_exact);
-    if (!arrive_last(ver.w.counters + kUserCounters + b, (unsigned)Hq))
+    if (!arrive_last(user_counter(ver.w, b), (unsigned)Hq))
       return;
     finalize_entry<D>(pa, ver.w, b, ver.o.o_approx, ver.o.o_exact,
                       ver.o.ratio, ver.o.commit, ver.o.o_committed,
@@ -1169,8 +1160,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
                             L.w.part_acc + ((size_t)it.slot * Hq + h0) * D);
   if (!approx) return;
   const unsigned n = (unsigned)(pa.nsink[it.b] + pa.nwin[it.b]);
-  if (!arrive_last(app.w.counters + kApproxCounters + it.b * pa.Hkv + it.g,
-                   n))
+  if (!arrive_last(approx_counter(app.w, it.b, pa.Hkv, it.g), n))
     return;
   approx_merge<D, G>(pa, app.w, app.o, it.b, it.g);
 }

@@ -14,14 +14,18 @@ constexpr int kMaxBatch = ALSPEC_MAX_BATCH;
 constexpr int kMaxKvHeads = ALSPEC_MAX_KV_HEADS;
 constexpr size_t kWsAlign = 256;
 // counters at the start of every workspace, independent of the shape, so a
-// workspace reused for another shape still finds them at zero:
-//   [kUserCounters, + kMaxBatch)        heads done (exact merge), per b
-//   [kApproxCounters, + kMaxBatch * kMaxKvHeads)
+// workspace reused for another shape still finds them at zero.  Each counter
+// has a 128-byte line of its own (kCounterStride words), so the arrivals of
+// different groups do not queue on one line's atomics:
+//   kUserCounters + b * kCounterStride      heads done (exact merge), per b
+//   kApproxCounters + (b * Hkv + g) * kCounterStride
 //                                       sink/window splits done (one-launch
 //                                       approximation), per (b, kv head)
+constexpr int kCounterStride = 32;
 constexpr int kUserCounters = 0;
-constexpr int kApproxCounters = kUserCounters + kMaxBatch;
-constexpr int kNumCounters = kApproxCounters + kMaxBatch * kMaxKvHeads;
+constexpr int kApproxCounters = kUserCounters + kMaxBatch * kCounterStride;
+constexpr int kNumCounters =
+    kApproxCounters + kMaxBatch * kMaxKvHeads * kCounterStride;
 constexpr size_t kCounterBytes = (kNumCounters * 4 + 255) / 256 * 256;
 
 // Everything a kernel needs to map a block index to its work; passed by
