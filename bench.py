@@ -83,12 +83,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "d458fdc600c5dc29877a6335dc4698fd"
-                     "6637442137857156cecbd75be45946e5",
+           "sha256": "1a530be6fd8b0a736d8ff7857fb4526f"
+                     "f921313f69b2d44b7dd64a0f2b4abdb7",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262902.9 * 1024 * 2.0, 871.3 * 1024 * 1.0),
-                     "partials_middle": (258199.3 * 1024 * 2.0,
+           "bytes": {"chain": (262864.6 * 1024 * 2.0, 871.0 * 1024 * 1.0),
+                     "partials_middle": (258173.7 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
