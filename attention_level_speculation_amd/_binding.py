@@ -83,6 +83,9 @@ _workspace_size = _sig("alspec_workspace_size", _PP,
 _plan_splits = _sig("alspec_plan_splits", _PP, _i32, _P, _P, _P, _i32,
                     ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                     ctypes.POINTER(_i32))
+_plan_splits_layers = _sig("alspec_plan_splits_layers", _PP, _i32, _P, _P,
+                           _P, _i32, ctypes.POINTER(_i32),
+                           ctypes.POINTER(_i32), ctypes.POINTER(_i32))
 _create = _sig("alspec_create", ctypes.c_int, ctypes.POINTER(_P))
 _destroy = _sig("alspec_destroy", _P)
 _sink_approx = _sig("alspec_sink_approx", _P, _PP, _P, _P, _P, _P, _P, _P,
@@ -161,21 +164,23 @@ def workspace_size(p):
     return int(n.value)
 
 
-def plan_splits(p, b):
+def plan_splits(p, b, layers=False):
     """[(kind, begin, end)] of batch entry b (kind 0 sink, 1 window, 2
-    middle), plus the (middle, window) split lengths."""
+    middle), plus the (middle, window) split lengths; layers=True gives the
+    plan of spec_decode_layers."""
+    fn, name = ((_plan_splits_layers, "alspec_plan_splits_layers") if layers
+                else (_plan_splits, "alspec_plan_splits"))
     cnt = _i32(0)
     t = _i32(0)
     tw = _i32(0)
-    _check(_plan_splits(ctypes.byref(p), b, None, None, None, 0,
-                        ctypes.byref(cnt), ctypes.byref(t), ctypes.byref(tw)),
-           "alspec_plan_splits")
+    _check(fn(ctypes.byref(p), b, None, None, None, 0, ctypes.byref(cnt),
+              ctypes.byref(t), ctypes.byref(tw)), name)
     n = cnt.value
     kind = (_i32 * max(1, n))()
     beg = (_i32 * max(1, n))()
     end = (_i32 * max(1, n))()
-    _check(_plan_splits(ctypes.byref(p), b, kind, beg, end, n,
-                        ctypes.byref(cnt), None, None), "alspec_plan_splits")
+    _check(fn(ctypes.byref(p), b, kind, beg, end, n, ctypes.byref(cnt), None,
+              None), name)
     return [(kind[i], beg[i], end[i]) for i in range(n)], (t.value, tw.value)
 
 

@@ -20,7 +20,8 @@ int pow2_floor(int x) {
 
 }  // namespace
 
-alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
+alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
+                        PlanFor use) {
   if (!p || !pa || !ws) return ALSPEC_ERR_INVALID_ARG;
   const int B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
   const int D = p->head_dim;
@@ -100,11 +101,13 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
     }
     T = (int)(lo * 64);
   }
-  // Window split length: the window is on the approximation's latency path,
-  // so it is cut into about 16 pieces that run side by side.
+  // Window split length: in a single step the window is on the
+  // approximation's latency path, so it is cut into about 16 pieces that run
+  // side by side; the layer-pipelined call cuts it into about 8 (fewer
+  // device-scope hand-offs beside its middle pass).
   int Tw = p->window_split_tokens;
   if (Tw == 0) {
-    Tw = max_win / 16;
+    Tw = max_win / (use == kPlanLayers ? 8 : 16);
     if (Tw < 64) Tw = 64;
     if (Tw > 512) Tw = 512;
     Tw = pow2_floor(Tw);

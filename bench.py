@@ -196,6 +196,7 @@ def main():
              "sink": (None, True), "fixsink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
+    Tw_layers = al.plan_splits(P["chain"], 0, layers=True)[1][1]
     n_mid = sum(1 for s in splits if s[0] == 2)
     mid_tokens = sum(e - b for k, b, e in splits if k == 2)
     a_tokens = sum(e - b for k, b, e in splits if k != 2)
@@ -503,7 +504,9 @@ def main():
             "batch": w0.B, "layers": nl, "num_q_heads": w0.Hq,
             "num_kv_heads": w0.Hkv, "head_dim": w0.D, "sink": w0.S,
             "window": w0.W, "lambda": w0.lam, "split_tokens": T,
-            "window_split_tokens": Tw, "middle_splits_per_head": n_mid,
+            "window_split_tokens": Tw,
+            "window_split_tokens_layer_pipelined": Tw_layers,
+            "middle_splits_per_head": n_mid,
             "generator": {"a": w0.const.a, "c_s": w0.const.c_s,
                           "tau_s": w0.const.tau_s, "c_n": w0.const.c_n,
                           "tau_n": w0.const.tau_n},

@@ -92,7 +92,13 @@ typedef struct {
                                   only through rounding order. */
   int32_t window_split_tokens; /* window split length; 0 = automatic: about
                                   1/16 of the longest window, a power of
-                                  two in [64, 512] */
+                                  two in [64, 512]; for
+                                  alspec_spec_decode_layers about 1/8 (its
+                                  approximation runs beside a middle pass,
+                                  where fewer splits mean fewer device-
+                                  scope hand-offs).  Set it to give the
+                                  layered and single calls the same plan,
+                                  and so the same bits. */
   int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
                       2 = pipelined (see alspec_spec_decode) */
 } alspec_params;
@@ -145,6 +151,15 @@ alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
                                  int32_t cap, int32_t *count,
                                  int32_t *split_tokens,
                                  int32_t *window_split_tokens);
+
+/* The same for the plan of alspec_spec_decode_layers, which differs only in
+ * the automatic window split length.  Its workspace need never exceeds
+ * alspec_workspace_size's. */
+alspec_status alspec_plan_splits_layers(const alspec_params *p, int32_t b,
+                                        int32_t *kind, int32_t *begin,
+                                        int32_t *end, int32_t cap,
+                                        int32_t *count, int32_t *split_tokens,
+                                        int32_t *window_split_tokens);
 
 /* Create a handle bound to HIP device `device`: the events the fused call
  * uses for cross-stream ordering, a 16-entry table of workspace events and

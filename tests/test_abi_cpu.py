@@ -149,6 +149,39 @@ def test_headline_plan_shape():
     _check_tiling(p, 0, 131072, 4, 2048)
 
 
+def test_layers_plan_cuts_the_window_in_half_as_many_splits():
+    """The layer-pipelined call's automatic window splits are about 1/8 of
+    the window (256 tokens at the headline shape, 8 per kv head) where a
+    single call's are about 1/16; both plans share the middle splits and
+    the sink, tile every context, and the layered one never has more slots,
+    so a workspace sized by alspec_workspace_size serves it."""
+    p = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1)
+    s1, (T1, Tw1) = al.plan_splits(p, 0)
+    s2, (T2, Tw2) = al.plan_splits(p, 0, layers=True)
+    assert (T1, Tw1, T2, Tw2) == (4032, 128, 4032, 256)
+    assert sum(1 for s in s2 if s[0] == 1) == 8
+    assert [s for s in s1 if s[0] != 1] == [s for s in s2 if s[0] != 1]
+    w2 = sorted((b, e) for k, b, e in s2 if k == 1)
+    assert w2[0][0] == 131072 - 2048 and w2[-1][1] == 131072
+    assert all(w2[i][1] == w2[i + 1][0] for i in range(len(w2) - 1))
+    # explicit lengths are taken as given by both
+    q = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1,
+                       window_split_tokens=96)
+    assert al.plan_splits(q, 0) == al.plan_splits(q, 0, layers=True)
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        B = int(rng.integers(1, 9))
+        L_cap = int(rng.choice([100, 5000, 131072]))
+        lens = [int(x) for x in rng.integers(1, L_cap + 1, size=B)]
+        W = int(rng.choice([1, 128, 1000, 4096, 20000]))
+        r = al.make_params(B, 8, 2, 64, L_cap, lens, "bf16", 4, W, 0.1)
+        for b in range(B):
+            a, (_, ta) = al.plan_splits(r, b)
+            c, (_, tc) = al.plan_splits(r, b, layers=True)
+            assert tc in (ta, 2 * ta) and len(c) <= len(a)
+            assert [x for x in a if x[0] != 1] == [x for x in c if x[0] != 1]
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_middle_split_length_fills_the_cus_once(seed):
     """The default middle split length is the shortest whole number of

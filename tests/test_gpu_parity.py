@@ -447,13 +447,24 @@ def _chain(handle, w, n_layers, n_ws=3, lam=None):
     return p, devs, wss, outs
 
 
+def _single_with_chain_plan(p):
+    """Params whose single calls use the plan spec_decode_layers takes for
+    p (its automatic window split is longer), so the two agree bit for
+    bit."""
+    q = type(p).from_buffer_copy(p)
+    q.window_split_tokens = al.plan_splits(p, 0, layers=True)[1][1]
+    assert al.plan_splits(q, 0)[1] == al.plan_splits(p, 0, layers=True)[1]
+    return q
+
+
 @pytest.mark.parametrize("shape,n_layers", [
     ("bf16_g4", 1), ("bf16_g4", 2), ("bf16_g4", 5), ("f32_g2", 4),
     ("bf16_g8_ragged", 3), ("f32_d64_g1_ragged", 4),
     ("bf16_d64_g4_tiny", 3)])
 def test_layers_chain_matches_single_calls(handle, shape, n_layers):
     """The layer-pipelined chain gives every layer exactly the outputs of a
-    single fused call on its inputs, with a ring of three workspaces: MFMA
+    single fused call on its inputs with the same plan, with a ring of three
+    workspaces (each sized for the single calls' automatic plan): MFMA
     and VALU split kernels, head dims 128 and 64, users whose context is
     shorter than the sink plus window (no middle) or a single token."""
     w = {"bf16_g4": gen.scaled(gen.llama8b_32k(), 6000),
@@ -473,8 +484,9 @@ def test_layers_chain_matches_single_calls(handle, shape, n_layers):
                                                                      outs))],
                           s)
     torch.cuda.synchronize()
+    ps = _single_with_chain_plan(p)
     for j, d in enumerate(devs):
-        ref = run_fused(al, handle, p, *d)
+        ref = run_fused(al, handle, ps, *d)
         for key in ref:
             assert np.array_equal(outs[j][key].cpu().numpy(), ref[key]), \
                 (j, key)
@@ -491,7 +503,8 @@ def test_layers_chain_full_size(handle, shape, n_layers):
     """The chain at full size with the automatic plan, the configuration
     the benchmark times (a launch with all three block ranges from the
     third layer on): every layer against the oracle, and bit for bit
-    against single fused calls on its inputs."""
+    against single fused calls on its inputs with the chain's plan (whose
+    window splits are twice as long as a single call's automatic ones)."""
     w = {"llama8b_128k": gen.llama8b_128k(needles=4),
          "llama70b_128k": gen.llama70b_128k()}[shape]
     p = al.params_for(w)
@@ -507,10 +520,12 @@ def test_layers_chain_full_size(handle, shape, n_layers):
     al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
                                       in enumerate(zip(devs, outs))])
     torch.cuda.synchronize()
+    ps = _single_with_chain_plan(p)
+    assert al.plan_splits(ps, 0)[1][1] == 2 * al.plan_splits(p, 0)[1][1]
     for j, d in enumerate(devs):
         got = {k_: v_.cpu().numpy() for k_, v_ in outs[j].items()}
         compare(got, refs[j], w.kv_dtype, w.lam, f"{shape} chain layer {j}")
-        single = run_fused(al, handle, p, *d)
+        single = run_fused(al, handle, ps, *d)
         for key in single:
             assert np.array_equal(got[key], single[key]), (j, key)
         print(f"[case] layer {j} ratio {got['ratio'][:4]}", flush=True)
