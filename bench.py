@@ -83,12 +83,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "1a530be6fd8b0a736d8ff7857fb4526f"
-                     "f921313f69b2d44b7dd64a0f2b4abdb7",
+           "sha256": "4f4b2c53ac9bbf13fe7fbb181536230f"
+                     "141763856b8e6e3c1570efb4863ae176",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262864.6 * 1024 * 2.0, 871.0 * 1024 * 1.0),
-                     "partials_middle": (258173.7 * 1024 * 2.0,
+           "bytes": {"chain": (262810.3 * 1024 * 2.0, 737.4 * 1024 * 1.0),
+                     "partials_middle": (258173.8 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
