@@ -1012,16 +1012,19 @@ __global__ __launch_bounds__(kThreads) void partials_kernel(
 }
 
 // Every split of the plan (sink, window and middle) in one launch: the
-// first blocks take the sink and window splits, the rest the middle ones.
+// first blocks take the long middle splits, one per CU, and the short sink
+// and window splits fill the slots left (dispatched first, the short ones
+// could take the slots of middle splits, which would then start late or
+// share a CU: 512 against 376 µs per layer at the 70B stack's shape).
 template <class KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void partials_all_kernel(
     PlanArgs pa, const float *__restrict__ q,
     const typename KV::elem *__restrict__ k,
     const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w) {
-  const int nA = pa.itemA_pre[pa.B];
+  const int nM = pa.itemM_pre[pa.B];
   const int idx = blockIdx.x;
   const Item it =
-      idx < nA ? decode_item(pa, true, idx) : decode_item(pa, false, idx - nA);
+      idx < nM ? decode_item(pa, false, idx) : decode_item(pa, true, idx - nM);
   const int Hq = pa.Hq;
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
   const int h0 = it.g * G;
@@ -1096,18 +1099,27 @@ __global__ __launch_bounds__(kThreads) void approx_combine_kernel(PlanArgs pa,
   approx_merge<D, G>(pa, w, o, blockIdx.x / pa.Hkv, blockIdx.x % pa.Hkv);
 }
 
-// Exact merge, verify and commit: one block per (entry, query head) merges
-// that head's stored sink+window state with its middle splits in one
-// memory round; the last head of an entry to finish issues the verdict.
-template <int D>
+// Exact merge of NH query heads (the plan's NHv) of one entry, verify and
+// commit: the block merges each head's stored sink+window state with its
+// middle splits in one memory round; the last block of the entry to finish
+// issues the verdict.  Shared by the fused call and the layer-pipelined
+// launch, so both give the same bits.
+template <int D, int NH>
+__device__ void verify_block(const PlanArgs &pa, const WsPtrs &w,
+                             const Outs &o, int idx) {
+  const int per = pa.Hq / NH;
+  const int b = idx / per, h0 = (idx % per) * NH;
+  exact_heads<D, NH>(pa, w, b, h0, o.o_approx, o.o_exact, o.lse_exact);
+  if (!arrive_last(user_counter(w, b), (unsigned)per)) return;
+  finalize_entry<D>(pa, w, b, o.o_approx, o.o_exact, o.ratio, o.commit,
+                    o.o_committed, o.lambda);
+}
+
+template <int D, int NH>
 __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
                                                                 WsPtrs w,
                                                                 Outs o) {
-  const int b = blockIdx.x / pa.Hq, h = blockIdx.x % pa.Hq;
-  exact_heads<D, 1>(pa, w, b, h, o.o_approx, o.o_exact, o.lse_exact);
-  if (!arrive_last(user_counter(w, b), (unsigned)pa.Hq)) return;
-  finalize_entry<D>(pa, w, b, o.o_approx, o.o_exact, o.ratio, o.commit,
-                    o.o_committed, o.lambda);
+  verify_block<D, NH>(pa, w, o, blockIdx.x);
 }
 
 // Second stage of the exact output from every split state of the plan:
@@ -1138,14 +1150,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
   int idx = blockIdx.x;
   if (idx >= nA + nM) {
     idx -= nA + nM;
-    const int b = idx / Hq, h = idx % Hq;
-    exact_heads<D, 1>(pa, ver.w, b, h, ver.o.o_approx, ver.o.o_exact,
-                      ver.o.lse_exact);
-    if (!arrive_last(user_counter(ver.w, b), (unsigned)Hq))
-      return;
-    finalize_entry<D>(pa, ver.w, b, ver.o.o_approx, ver.o.o_exact,
-                      ver.o.ratio, ver.o.commit, ver.o.o_committed,
-                      ver.o.lambda);
+    if (pa.NHv == 4)
+      verify_block<D, 4>(pa, ver.w, ver.o, idx);
+    else
+      verify_block<D, 1>(pa, ver.w, ver.o, idx);
     return;
   }
   const bool approx = idx < nA;
@@ -1165,12 +1173,14 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
   approx_merge<D, G>(pa, app.w, app.o, it.b, it.g);
 }
 
-template <int D>
+template <int D, int NH>
 __global__ __launch_bounds__(kThreads) void lse_middle_kernel(
     PlanArgs pa, WsPtrs w, float *__restrict__ o_exact,
     float *__restrict__ lse_exact) {
-  exact_heads<D, 1, false>(pa, w, blockIdx.x / pa.Hq, blockIdx.x % pa.Hq,
-                           nullptr, o_exact, lse_exact);
+  const int per = pa.Hq / NH;
+  exact_heads<D, NH, false>(pa, w, blockIdx.x / per,
+                            (blockIdx.x % per) * NH, nullptr, o_exact,
+                            lse_exact);
 }
 
 __global__ __launch_bounds__(kThreads) void verify_kernel(
@@ -1309,7 +1319,7 @@ hipError_t chain_kg(const PlanArgs &pa, const ChainLayer *mid,
                     const ChainLayer *app, const ChainLayer *ver,
                     float sm_log2, hipStream_t s) {
   const ChainLayer none{};
-  const int nV = ver ? pa.B * pa.Hq : 0;
+  const int nV = ver ? pa.B * pa.Hq / pa.NHv : 0;
   const int nA = app ? pa.itemA_pre[pa.B] : 0;
   const int nM = mid ? pa.itemM_pre[pa.B] : 0;
   if (nV + nA + nM == 0) return hipSuccess;
@@ -1395,10 +1405,15 @@ hipError_t launch_approx_combine(const PlanArgs &pa, const WsPtrs &w,
 
 hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
                                const Outs &o, hipStream_t s) {
-  dim3 grid(pa.B * pa.Hq), block(kThreads);
+  dim3 grid(pa.B * pa.Hq / pa.NHv), block(kThreads);
+  if (pa.NHv == 4) {
+    if (pa.D == 128)
+      return launch(merge_verify_kernel<128, 4>, grid, block, s, pa, w, o);
+    return launch(merge_verify_kernel<64, 4>, grid, block, s, pa, w, o);
+  }
   if (pa.D == 128)
-    return launch(merge_verify_kernel<128>, grid, block, s, pa, w, o);
-  return launch(merge_verify_kernel<64>, grid, block, s, pa, w, o);
+    return launch(merge_verify_kernel<128, 1>, grid, block, s, pa, w, o);
+  return launch(merge_verify_kernel<64, 1>, grid, block, s, pa, w, o);
 }
 
 hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
@@ -1409,11 +1424,18 @@ hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
   const Outs none{};
   const hipError_t e = launch_approx_combine(pa, w, none, s);
   if (e != hipSuccess) return e;
-  dim3 grid(pa.B * pa.Hq), block(kThreads);
-  if (pa.D == 128)
-    return launch(lse_middle_kernel<128>, grid, block, s, pa, w, o_exact,
+  dim3 grid(pa.B * pa.Hq / pa.NHv), block(kThreads);
+  if (pa.NHv == 4) {
+    if (pa.D == 128)
+      return launch(lse_middle_kernel<128, 4>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
+    return launch(lse_middle_kernel<64, 4>, grid, block, s, pa, w, o_exact,
                   lse_exact);
-  return launch(lse_middle_kernel<64>, grid, block, s, pa, w, o_exact,
+  }
+  if (pa.D == 128)
+    return launch(lse_middle_kernel<128, 1>, grid, block, s, pa, w, o_exact,
+                  lse_exact);
+  return launch(lse_middle_kernel<64, 1>, grid, block, s, pa, w, o_exact,
                 lse_exact);
 }
 

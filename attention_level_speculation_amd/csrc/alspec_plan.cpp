@@ -101,15 +101,24 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
     }
     T = (int)(lo * 64);
   }
-  // Window split length: in a single step the window is on the
-  // approximation's latency path, so it is cut into about 16 pieces that run
-  // side by side; the layer-pipelined call cuts it into about 8 (fewer
-  // device-scope hand-offs beside its middle pass).
+  // Window split length: the windows of all (entry, kv head) pairs are cut
+  // into about 128 splits in all for a single step, whose approximation is
+  // on the latency path and runs side by side on half the CUs, and into
+  // about 64 for the layer-pipelined call, whose approximation runs beside
+  // a middle pass.  Every split ends in a device-scope hand-off, and those
+  // queue per XCD, so more splits than that cost more than they save.  A
+  // power of two from 64 to 1024 tokens: a longer split streams for long on
+  // one CU (beside a middle split, in the layer-pipelined launch).
   int Tw = p->window_split_tokens;
   if (Tw == 0) {
-    Tw = max_win / (use == kPlanLayers ? 8 : 16);
+    int pairs = 0;
+    for (int b = 0; b < B; ++b)
+      if (pa->L[b] > pa->w_begin[b]) pairs += Hkv;
+    const int target = use == kPlanLayers ? 64 : 128;
+    const int pieces = pairs > 0 && pairs < target ? target / pairs : 1;
+    Tw = max_win / pieces;
     if (Tw < 64) Tw = 64;
-    if (Tw > 512) Tw = 512;
+    if (Tw > 1024) Tw = 1024;
     Tw = pow2_floor(Tw);
   }
   pa->T = T;
@@ -130,6 +139,15 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
     pa->itemM_pre[b + 1] = pa->itemM_pre[b] + pa->nmid[b] * Hkv;
   }
   pa->total_slots = slots;
+  // Query heads per exact-merge block: 4 where there are many (entry, head)
+  // pairs, so fewer blocks take the device-scope hand-off of the verify,
+  // as long as every head's middle states still fit one memory round of
+  // the merge (2048 / D slots for 4 heads).  The choice sets the merge's
+  // summation order, so every merging kernel takes it from here.
+  int max_mid = 0;
+  for (int b = 0; b < B; ++b)
+    if (pa->nmid[b] > max_mid) max_mid = pa->nmid[b];
+  pa->NHv = (Hq % 4 == 0 && B * Hq >= 128 && max_mid <= 2048 / D) ? 4 : 1;
 
   size_t off = 0;
   ws->off_counters = off;

@@ -34,6 +34,7 @@ struct PlanArgs {
   int B, Hq, Hkv, G, D, L_cap;
   int T;   // middle split length (tokens)
   int Tw;  // window split length (tokens)
+  int NHv; // query heads per exact-merge block (1 or 4)
   int total_slots;
   int L[kMaxBatch];
   int s_end[kMaxBatch];    // sink = [0, s_end)
@@ -60,10 +61,11 @@ constexpr int kNominalCUs = 256;
 
 // Which call the plan is for: the automatic window split length differs.
 // A single step has its approximation on the latency path and cuts the
-// window into about 16 splits that run side by side; the layer-pipelined
-// call runs the approximation beside a middle pass, where each split's
-// device-scope hand-off costs throughput, and cuts it into about 8.  The
-// step plan never has fewer slots, so its workspace size serves both.
+// windows into about 128 splits in all that run side by side; the
+// layer-pipelined call runs the approximation beside a middle pass, where
+// each split's device-scope hand-off costs throughput, and cuts them into
+// about 64.  The step plan never has fewer slots, so its workspace size
+// serves both.
 enum PlanFor { kPlanStep = 0, kPlanLayers = 1 };
 
 // Validate `p` and fill the plan.  Returns ALSPEC_OK or the status to report.

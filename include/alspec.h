@@ -90,15 +90,17 @@ typedef struct {
                                   256 when the (entry, kv head) pairs are
                                   more.  Results depend on the split plan
                                   only through rounding order. */
-  int32_t window_split_tokens; /* window split length; 0 = automatic: about
-                                  1/16 of the longest window, a power of
-                                  two in [64, 512]; for
-                                  alspec_spec_decode_layers about 1/8 (its
-                                  approximation runs beside a middle pass,
-                                  where fewer splits mean fewer device-
-                                  scope hand-offs).  Set it to give the
-                                  layered and single calls the same plan,
-                                  and so the same bits. */
+  int32_t window_split_tokens; /* window split length; 0 = automatic: the
+                                  longest window over (128 / pairs),
+                                  rounded down to a power of two from 64
+                                  to 1024 tokens, pairs being the (entry,
+                                  kv head) pairs with a window; for
+                                  alspec_spec_decode_layers over (64 /
+                                  pairs) (its approximation runs beside a
+                                  middle pass, where fewer splits mean
+                                  fewer device-scope hand-offs).  Set it
+                                  to give the layered and single calls the
+                                  same plan, and so the same bits. */
   int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
                       2 = pipelined (see alspec_spec_decode) */
 } alspec_params;

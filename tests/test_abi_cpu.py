@@ -150,11 +150,12 @@ def test_headline_plan_shape():
 
 
 def test_layers_plan_cuts_the_window_in_half_as_many_splits():
-    """The layer-pipelined call's automatic window splits are about 1/8 of
-    the window (256 tokens at the headline shape, 8 per kv head) where a
-    single call's are about 1/16; both plans share the middle splits and
-    the sink, tile every context, and the layered one never has more slots,
-    so a workspace sized by alspec_workspace_size serves it."""
+    """The automatic window splits number about 128 over all (entry, kv
+    head) pairs for a single call and about 64 for the layer-pipelined call
+    (at the headline shape, 16 and 8 per kv head: 128 and 256 tokens); both
+    plans share the middle splits and the sink, tile every context, and the
+    layered one never has more slots, so a workspace sized by
+    alspec_workspace_size serves it."""
     p = al.make_params(1, 32, 8, 128, 131072, [131072], "bf16", 4, 2048, 0.1)
     s1, (T1, Tw1) = al.plan_splits(p, 0)
     s2, (T2, Tw2) = al.plan_splits(p, 0, layers=True)
@@ -178,8 +179,31 @@ def test_layers_plan_cuts_the_window_in_half_as_many_splits():
         for b in range(B):
             a, (_, ta) = al.plan_splits(r, b)
             c, (_, tc) = al.plan_splits(r, b, layers=True)
-            assert tc in (ta, 2 * ta) and len(c) <= len(a)
+            assert tc >= ta and tc % ta == 0 and len(c) <= len(a)
             assert [x for x in a if x[0] != 1] == [x for x in c if x[0] != 1]
+
+
+@pytest.mark.parametrize("B,Hkv,W,tw_step,tw_layers", [
+    (1, 8, 2048, 128, 256),     # Llama-3-8B at 128K: 16 and 8 per kv head
+    (4, 8, 4096, 1024, 1024),   # Llama-3-70B stack, 4 users: 4 each (cap)
+    (1, 8, 1024, 64, 128),      # Llama-3-8B at 32K
+    (8, 8, 2048, 1024, 1024),   # 8 users: 2 per (user, kv head) (cap)
+    (2, 8, 2048, 256, 512),     # 2 users: 8 and 4 per (user, kv head)
+    (64, 8, 2048, 1024, 1024),  # more pairs than splits: at most 1024
+    (1, 8, 128, 64, 64),        # short window: at least 64 tokens
+])
+def test_automatic_window_split_targets_a_split_count(B, Hkv, W, tw_step,
+                                                      tw_layers):
+    """The automatic window split is the power of two (64 to 1024) at or
+    below the longest window over (128 / pairs) for a single call and over
+    (64 / pairs) for the layer-pipelined call, pairs being the (entry, kv
+    head) pairs with a window."""
+    p = al.make_params(B, Hkv * 4, Hkv, 128, 131072, [131072] * B, "bf16",
+                       4, W, 0.1)
+    assert al.plan_splits(p, 0)[1][1] == tw_step
+    assert al.plan_splits(p, 0, layers=True)[1][1] == tw_layers
+    n = sum(1 for s in al.plan_splits(p, 0)[0] if s[0] == 1) * B * Hkv
+    assert n <= max(128, B * Hkv * -(-W // 1024))
 
 
 @pytest.mark.parametrize("seed", range(30))
