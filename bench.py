@@ -83,11 +83,11 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "4f4b2c53ac9bbf13fe7fbb181536230f"
-                     "141763856b8e6e3c1570efb4863ae176",
+           "sha256": "482ef486341e23f7631ba26711724e86"
+                     "0b6d4f8b3b9f009dea1204f6a31912b9",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262810.3 * 1024 * 2.0, 737.4 * 1024 * 1.0),
+           "bytes": {"chain": (262834.2 * 1024 * 2.0, 737.4 * 1024 * 1.0),
                      "partials_middle": (258173.8 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
