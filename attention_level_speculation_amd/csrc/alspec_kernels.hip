@@ -845,10 +845,11 @@ __device__ __forceinline__ Item decode_item(const PlanArgs &pa,
 }
 
 // Slots merged per thread per memory round in the merges of the sink and
-// window states.  The plan gives 16 window splits plus one sink split
-// for windows of 1024 to 8192 tokens, and the merge's two slot
-// groups per head then take all 17 in one round (at 8 a second round and a
-// separate max pass would each add a dependent round trip).
+// window states.  A single call's automatic plan gives one entry with 8 kv
+// heads (the Llama-3 shapes) 16 window splits plus one sink split, and the
+// merge's two slot groups per head take up to 18 in one round (at 8, the
+// 17th slot would add a separate max pass and a second round, each a
+// dependent round trip).
 constexpr int kMergeRoundA = 9;
 // ... and in the exact merges (many middle splits).
 constexpr int kMergeRoundM = 8;
@@ -1122,12 +1123,8 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
   verify_block<D, NH>(pa, w, o, blockIdx.x);
 }
 
-// Second stage of the exact output from every split state of the plan:
-// one block per (entry, query head) merges the head's middle states onto
-// the merged sink+window state, as the fused call's exact merge does (so
-// both give the same bits).
 // Layer-pipelined launch: one grid holds three disjoint block ranges, all
-// resident at once (three 4-wave blocks fit a CU):
+// resident at once (three or four 4-wave blocks fit a CU):
 //   [0, nA)              the whole approximation of layer j+1, one block
 //                        per sink or window split, the last of an (entry,
 //                        kv head) to finish merging the group's states,
@@ -1173,6 +1170,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
   approx_merge<D, G>(pa, app.w, app.o, it.b, it.g);
 }
 
+// Second stage of the exact output from every split state of the plan:
+// one block per NH query heads of an entry (the plan's NHv) merges each
+// head's middle states onto the merged sink+window state, as the fused
+// call's exact merge does (so both give the same bits).
 template <int D, int NH>
 __global__ __launch_bounds__(kThreads) void lse_middle_kernel(
     PlanArgs pa, WsPtrs w, float *__restrict__ o_exact,
