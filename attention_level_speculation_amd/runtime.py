@@ -5,14 +5,16 @@ Approach: the post-attention ops run speculatively while exact attention
 is computed, and a relative L2 check commits or discards them).
 
 Scheduling only: every step is a call of the C ABI (the attention step,
-alspec_spec_decode, and the post-attention operators,
-alspec_post_attention), enqueued on two HIP streams.  Whether a layer's
-replay does any work is decided on the device: the replay kernels read the
-layer's commit flag and end at once where it is set, so the sequence of
-launches is static and the work dynamic.  The step is issued eagerly: its
-two streams wait on each other in turn, and capturing that into a HIP
-graph ended in a host segmentation fault inside hipStreamEndCapture with
-the HIP runtime torch loads.
+alspec_spec_decode or its separate calls, and the post-attention
+operators, alspec_post_attention), enqueued on HIP streams.  Whether a
+layer's replay does any work is decided on the device: the replay kernels
+read the layer's commit flag and end at once where it is set, so the
+sequence of launches is static and the work dynamic.  The two-stream form
+is issued eagerly: its two streams wait on each other in turn, and
+capturing that into a HIP graph ended in a host segmentation fault inside
+hipStreamEndCapture with the HIP runtime torch loads.  The one-stream form
+(one_stream=True) issues the same work in dependency order on one stream,
+so the whole stack of layers captures into one HIP graph.
 
 Per layer l, with q_l the first Hq*D entries of the previous layer's QKV
 projection (one decode token, batch 1):
@@ -28,6 +30,14 @@ so layer l+1 starts from the committed output of layer l: o_approx where
 the verify committed it, else o_exact.  The result equals the plain
 sequence "alspec_spec_decode, then post-attention on o_committed" bit for
 bit (model_step with speculative=False).
+
+The one-stream form, per layer on stream_exact: alspec_sink_approx, the
+post-attention work on o_approx, alspec_flash_decode_exact over the middle
+splits, alspec_lse_combine, alspec_verify, then the replay on o_exact with
+the commit flag as skip flag.  The speculative work runs before the exact
+pass instead of beside it (on one GPU both stream from the same HBM, so
+running them side by side buys nothing), and the result is again the
+committed output's post-attention work.
 """
 from . import _binding as B_
 
@@ -52,7 +62,8 @@ def q_view(p, qkv):
 
 
 def model_step(h, p, pp, q0, layers, ws_attn, ws_post_a, ws_post_b,
-               stream_approx, stream_exact, speculative=True, exact_only=False):
+               stream_approx, stream_exact, speculative=True, exact_only=False,
+               one_stream=False):
     """Enqueue one decode token through `layers` (list of ModelLayer).
 
     p: attention params (batch 1; p.overlap is ignored: the sequential mode
@@ -61,8 +72,10 @@ def model_step(h, p, pp, q0, layers, ws_attn, ws_post_a, ws_post_b,
     workspaces of the two streams.  speculative=False runs the same
     arithmetic as one sequence on stream_exact; exact_only=True runs exact
     attention (every split, no approximation or verify) and the
-    post-attention work on its output, the non-speculative baseline.
-    Layer l's query is layers[l-1].qkv_out's query part."""
+    post-attention work on its output, the non-speculative baseline;
+    one_stream=True (with speculative) runs the speculative form on
+    stream_exact alone, in an order a stream capture can record.  Layer l's
+    query is layers[l-1].qkv_out's query part."""
     if p.batch != 1 or pp.batch != 1:
         raise ValueError("the chained step takes one decode token (batch 1)")
     p0 = B_.Params.from_buffer_copy(p)
@@ -78,6 +91,19 @@ def model_step(h, p, pp, q0, layers, ws_attn, ws_post_a, ws_post_b,
             B_.post_attention(h, pp, layer.weights, o["o_exact"].view(1, -1),
                               layer.h_in, layer.h_out, layer.qkv_out,
                               ws_post_b, stream=se)
+        elif speculative and one_stream:
+            B_.sink_approx(h, p0, q, layer.k, layer.v, o["o_approx"],
+                           o["lse_approx"], ws_attn, se)
+            B_.post_attention(h, pp, layer.weights, o["o_approx"].view(1, -1),
+                              layer.h_in, layer.h_out, layer.qkv_out,
+                              ws_post_a, stream=se)
+            B_.flash_decode_exact(h, p0, q, layer.k, layer.v, 0, ws_attn, se)
+            B_.lse_combine(h, p0, ws_attn, o["o_exact"], o["lse_exact"], se)
+            B_.verify(h, p0, o["o_approx"], o["o_exact"], o["ratio"],
+                      o["commit"], o["o_committed"], se)
+            B_.post_attention(h, pp, layer.weights, o["o_exact"].view(1, -1),
+                              layer.h_in, layer.h_out, layer.qkv_out,
+                              ws_post_b, skip=o["commit"], stream=se)
         elif speculative:
             B_.spec_decode(h, p0, q, layer.k, layer.v, o, ws_attn,
                            stream_approx=sa, stream_exact=se)

@@ -13,9 +13,14 @@ work and replay on discard (attention_level_speculation_amd.runtime).
   after 3 layers with fp32 KV (each attention output is within ~1e-6 of
   the oracle's and each post-attention step within ~1e-7; chaining through
   the layers' queries amplifies this by at most a few hundred).
-- A captured graph of the speculative step replaying to the eager result
-  is skipped: capture crashed the host inside the HIP runtime (see the
-  test's reason).
+- The one-stream speculative form (speculative work on o_approx before
+  the exact pass, replay gated by the commit flag) gives the committed
+  sequence's result, matches the oracle chain where the flags are not in
+  doubt, and, captured into one HIP graph, replays to the eager result
+  bit for bit, three times with eager work in between.
+- A captured graph of the two-stream speculative step replaying to the
+  eager result is skipped: capture crashed the host inside the HIP runtime
+  (see the test's reason).
 """
 import numpy as np
 import pytest
@@ -120,6 +125,22 @@ def test_speculative_equals_committed_sequence(handle, lam):
         assert flags == [1] * N_LAYERS
 
 
+@pytest.mark.parametrize("lam", [0.0, 0.1, 0.5, float("inf")])
+def test_one_stream_equals_committed_sequence(handle, lam):
+    """The one-stream form runs the separate calls (approximation, middle
+    pass, combine, verify), whose outputs are the fused call's; where the
+    flags agree the final residual and QKV equal the committed sequence's
+    bit for bit."""
+    w, ps, host = _setup(lam)
+    dev = _device(w, ps, host, lam)
+    print(f"[case] model one stream lam={lam}", flush=True)
+    hs, qs, flags = _run(handle, dev, speculative=True, one_stream=True)
+    hq, qq, flags2 = _run(handle, dev, speculative=False)
+    print(f"[case] commits {flags} / {flags2}", flush=True)
+    assert flags == flags2
+    assert np.array_equal(hs, hq) and np.array_equal(qs, qq)
+
+
 def _oracle_chain(w, ps, host, lam):
     q = host["kv"][0][0].astype(np.float64)
     h = host["h0"].astype(np.float64)
@@ -144,6 +165,52 @@ def test_chain_matches_oracle_chain(handle, lam):
     print(f"[case] chain vs oracle lam={lam}: h {eh:.2e} qkv {eq:.2e}",
           flush=True)
     assert eh <= 1e-4 and eq <= 1e-4
+
+
+@pytest.mark.parametrize("lam", [0.0, float("inf")])
+def test_one_stream_matches_oracle_chain(handle, lam):
+    w, ps, host = _setup(lam)
+    dev = _device(w, ps, host, lam)
+    hg, qg, _ = _run(handle, dev, speculative=True, one_stream=True)
+    ho, qo = _oracle_chain(w, ps, host, lam)
+    eh = np.linalg.norm(hg - ho) / np.linalg.norm(ho)
+    eq = np.linalg.norm(qg - qo) / np.linalg.norm(qo)
+    print(f"[case] one-stream chain vs oracle lam={lam}: h {eh:.2e} "
+          f"qkv {eq:.2e}", flush=True)
+    assert eh <= 1e-4 and eq <= 1e-4
+
+
+def test_one_stream_graph_replays_match_eager(handle):
+    """The one-stream step over all layers captured into one HIP graph:
+    three replays, each after eager work on the same buffers, give the
+    eager step's bits (the commit flags at lambda 0.1 mix)."""
+    w, ps, host = _setup(0.1)
+    dev = _device(w, ps, host, 0.1)
+    want_h, want_q, want_f = _run(handle, dev, speculative=True,
+                                  one_stream=True)
+    p, pp, q0, layers, ws, _ = dev
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    print("[case] capture one-stream step", flush=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        rt.model_step(handle, p, pp, q0, layers, *ws, cap, cap,
+                      speculative=True, one_stream=True)
+    for rep in range(3):
+        _run(handle, dev, speculative=False)       # eager work in between
+        for l_ in layers:
+            l_.h_out.fill_(float("nan"))
+            l_.qkv_out.fill_(float("nan"))
+            l_.out["commit"].fill_(7)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            g.replay()
+        torch.cuda.synchronize()
+        print(f"[case] replay {rep}", flush=True)
+        assert np.array_equal(layers[-1].h_out.cpu().numpy(), want_h), rep
+        assert np.array_equal(layers[-1].qkv_out.cpu().numpy(), want_q), rep
+        assert [int(l_.out["commit"][0].item()) for l_ in layers] == want_f
 
 
 @pytest.mark.skip(reason="capturing this step ended in a host segmentation "
