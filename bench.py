@@ -654,17 +654,23 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
     step on the resident 128K KV, then the post-attention operators with
     seeded random bf16 weights (o_proj, RMSNorm + gated MLP, down, RMSNorm
     + next QKV; 416 MiB per layer), layer l+1's query from layer l's QKV.
-    Timed eagerly (the two-stream step cannot be captured, see the runtime
-    module), by wall clock between synchronisations, in three forms:
+    Timed by wall clock between synchronisations, in four forms:
       exact_only      exact attention, then post-attention on its output
       spec_sequence   attention step with verify, then post-attention on
                       the committed output, one stream
       spec_overlap    the same result with the post-attention work run on
                       o_approx beside the exact pass and replayed on o_exact
-                      after a discard (runtime.model_step)
-    The last at lambda 0.10 and, to bracket it, at +inf (every layer
-    commits) and 0 (every layer discards).  Also the post-attention kernels
-    alone against the HBM roofline (HIP events around back-to-back layers).
+                      after a discard (runtime.model_step; eager: the two-
+                      stream step cannot be captured, see the runtime
+                      module)
+      spec_one_stream_graph
+                      the speculative work on o_approx before the exact
+                      pass, on one stream, all layers captured as one HIP
+                      graph
+    The speculative forms at lambda 0.10 and, to bracket them, at +inf
+    (every layer commits) and 0 (every layer discards).  Also the
+    post-attention kernels alone against the HBM roofline (HIP events
+    around back-to-back layers).
     """
     import torch
 
@@ -725,20 +731,35 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
         "algorithmic_bytes_per_layer": ps.weight_bytes(),
         "us_per_layer": us, "layers_timed": reps}
 
-    def run(lam, **kw):
+    def run(lam, graph=False, **kw):
         p = al.params_for(w, lam=lam)
         outs = [al.alloc_outputs(p, dev) for _ in range(nl)]
         layers = [rt.ModelLayer(K[l], V[l], structs[l], outs[l], hs[l],
                                 hs[l + 1], qkvs[l]) for l in range(nl)]
         ws = al.alloc_workspace(p, dev)
 
-        def step():
+        def issue():
             sa.wait_stream(cur)
             se.wait_stream(cur)
             rt.model_step(h, p, pp, Q[0], layers, ws, wsp[0], wsp[1], sa, se,
                           **kw)
             cur.wait_stream(sa)
             cur.wait_stream(se)
+        step = issue
+        if graph:
+            # the one-stream form over all layers as one HIP graph
+            issue()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=se):
+                rt.model_step(h, p, pp, Q[0], layers, ws, wsp[0], wsp[1],
+                              se, se, **kw)
+
+            def step():
+                se.wait_stream(cur)
+                with torch.cuda.stream(se):
+                    g.replay()
+                cur.wait_stream(se)
         step()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -756,6 +777,12 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
     res["spec_overlap"] = run(w.lam, speculative=True)
     res["spec_overlap_all_commit"] = run(float("inf"), speculative=True)
     res["spec_overlap_all_discard"] = run(0.0, speculative=True)
+    res["spec_one_stream_graph"] = run(w.lam, graph=True, speculative=True,
+                                       one_stream=True)
+    res["spec_one_stream_graph_all_commit"] = run(
+        float("inf"), graph=True, speculative=True, one_stream=True)
+    res["spec_one_stream_graph_all_discard"] = run(
+        0.0, graph=True, speculative=True, one_stream=True)
     return res
 
 
