@@ -1149,6 +1149,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
     idx -= nA + nM;
     if (pa.NHv == 4)
       verify_block<D, 4>(pa, ver.w, ver.o, idx);
+    else if (pa.NHv == 2)
+      verify_block<D, 2>(pa, ver.w, ver.o, idx);
     else
       verify_block<D, 1>(pa, ver.w, ver.o, idx);
     return;
@@ -1412,6 +1414,11 @@ hipError_t launch_merge_verify(const PlanArgs &pa, const WsPtrs &w,
       return launch(merge_verify_kernel<128, 4>, grid, block, s, pa, w, o);
     return launch(merge_verify_kernel<64, 4>, grid, block, s, pa, w, o);
   }
+  if (pa.NHv == 2) {
+    if (pa.D == 128)
+      return launch(merge_verify_kernel<128, 2>, grid, block, s, pa, w, o);
+    return launch(merge_verify_kernel<64, 2>, grid, block, s, pa, w, o);
+  }
   if (pa.D == 128)
     return launch(merge_verify_kernel<128, 1>, grid, block, s, pa, w, o);
   return launch(merge_verify_kernel<64, 1>, grid, block, s, pa, w, o);
@@ -1431,6 +1438,13 @@ hipError_t launch_lse_combine(const PlanArgs &pa, const WsPtrs &w,
       return launch(lse_middle_kernel<128, 4>, grid, block, s, pa, w, o_exact,
                     lse_exact);
     return launch(lse_middle_kernel<64, 4>, grid, block, s, pa, w, o_exact,
+                  lse_exact);
+  }
+  if (pa.NHv == 2) {
+    if (pa.D == 128)
+      return launch(lse_middle_kernel<128, 2>, grid, block, s, pa, w, o_exact,
+                    lse_exact);
+    return launch(lse_middle_kernel<64, 2>, grid, block, s, pa, w, o_exact,
                   lse_exact);
   }
   if (pa.D == 128)

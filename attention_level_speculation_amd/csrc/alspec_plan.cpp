@@ -139,15 +139,18 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
     pa->itemM_pre[b + 1] = pa->itemM_pre[b] + pa->nmid[b] * Hkv;
   }
   pa->total_slots = slots;
-  // Query heads per exact-merge block: 4 where there are many (entry, head)
-  // pairs, so fewer blocks take the device-scope hand-off of the verify,
-  // as long as every head's middle states still fit one memory round of
-  // the merge (2048 / D slots for 4 heads).  The choice sets the merge's
-  // summation order, so every merging kernel takes it from here.
+  // Query heads per exact-merge block: the most of 4, 2 and 1 for which
+  // every head's middle states still fit one memory round of the merge
+  // (8192 / (NH D) slots), 4 only where there are many (entry, head)
+  // pairs.  Fewer blocks then take the verify's device-scope hand-off.  The
+  // choice sets the merge's summation order, so every merging kernel takes
+  // it from here.
   int max_mid = 0;
   for (int b = 0; b < B; ++b)
     if (pa->nmid[b] > max_mid) max_mid = pa->nmid[b];
-  pa->NHv = (Hq % 4 == 0 && B * Hq >= 128 && max_mid <= 2048 / D) ? 4 : 1;
+  pa->NHv = (Hq % 4 == 0 && B * Hq >= 128 && max_mid <= 2048 / D) ? 4
+            : (Hq % 2 == 0 && max_mid <= 4096 / D)                  ? 2
+                                                                    : 1;
 
   size_t off = 0;
   ws->off_counters = off;

@@ -34,7 +34,7 @@ struct PlanArgs {
   int B, Hq, Hkv, G, D, L_cap;
   int T;   // middle split length (tokens)
   int Tw;  // window split length (tokens)
-  int NHv; // query heads per exact-merge block (1 or 4)
+  int NHv; // query heads per exact-merge block (1, 2 or 4)
   int total_slots;
   int L[kMaxBatch];
   int s_end[kMaxBatch];    // sink = [0, s_end)

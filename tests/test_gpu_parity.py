@@ -153,12 +153,15 @@ EDGE = [
     ("max_kv_heads", 1, 64, 64, 128, [1700], "bf16", 4, 128, 0, 0),
     # four query heads per exact-merge block (at least 128 (user, head)
     # pairs, every head's middle states in one merge round: up to 32 at
-    # D = 64, 16 at D = 128), and one per block where a head has more
+    # D = 64, 16 at D = 128), and one per block where a head has more than
+    # a two-head round holds (32 at D = 128)
     ("nh4_d64_f32", 8, 16, 4, 64, [3000, 2500, 4000, 1800, 3500, 2200, 2900,
                                    4096], "f32", 4, 256, 256, 0),
     ("nh4_d128_bf16", 4, 32, 8, 128, [6000, 5000, 7000, 6500], "bf16", 4,
      512, 512, 0),
     ("nh1_many_middle", 4, 32, 8, 128, [9000] * 4, "bf16", 4, 256, 256, 0),
+    # two per block (32 slots at D = 128) for a single entry
+    ("nh2_d128_bf16", 1, 32, 8, 128, [40000], "bf16", 4, 1024, 2048, 0),
 ]
 
 
