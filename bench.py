@@ -83,12 +83,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "4ccbaa941b4507ff5af27bd0921517fe"
-                     "f360e8f001073780f836f759f218d50f",
+           "sha256": "2c371cce95c560182d5a32bde2a79a4b"
+                     "319d744a5eadc4ce295e990688aeb588",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262833.2 * 1024 * 2.0, 737.4 * 1024 * 1.0),
-                     "partials_middle": (258173.8 * 1024 * 2.0,
+           "bytes": {"chain": (262824.0 * 1024 * 2.0, 735.9 * 1024 * 1.0),
+                     "partials_middle": (258173.7 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
