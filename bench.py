@@ -43,9 +43,11 @@ Schedules (overlap modes of the library):
                 the static approximation on the odd layers, exact attention
                 (as in the exact-only baseline) on the even ones, as a graph.
 The headline value is the throughput of the fastest speculative schedule
-(named in config.schedule); those all compute the same outputs.  The
-baselines are reported beside it, with each one's output error against
-exact attention on the same inputs.
+(named in config.schedule).  They compute the same outputs; the
+layer-pipelined ones do so with their own automatic window splits (about
+half as many; config.window_split_tokens_layer_pipelined), so they agree
+with the others up to rounding.  The baselines are reported beside it,
+with each one's output error against exact attention on the same inputs.
 
 Also reported: KV GB/s of the headline schedule's dominant kernel against
 the HBM peak (for the layer-pipelined schedules its kernel in the steady
@@ -54,8 +56,12 @@ beside it the exact split-K kernel alone, from HIP events around
 back-to-back launches over all resident layers), per-kernel HIP events in
 eagerly issued steps of the schedules, the speculation
 hit rate per density, each layer's time to its approximate and to its
-verified output and the critical-path time a commit saves, the HBM probe,
-and the CPU oracle timed on a bounded sample of the same layers.
+verified output and the critical-path time a commit saves, the chained
+decode step with the post-attention operators (model_step: eager two-stream
+overlap and the one-stream form as one HIP graph, with the operators'
+own HBM roofline), a two-GPU projection from the measured durations, the
+HBM probe, and the CPU oracle timed on a bounded sample of the same
+layers.
 """
 import argparse
 import ctypes
