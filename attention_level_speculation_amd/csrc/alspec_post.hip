@@ -17,7 +17,12 @@
 // One wave owns kRows (4, 2 or 1, chosen per matrix so that the blocks
 // fill whole rounds of the CUs) consecutive weight rows and walks the
 // shared dimension K in 16-byte chunks (8 bf16), lane l taking chunks l,
-// l + 64, ...; U chunks per row are loaded before any is used.  The
+// l + 64, ...; U chunks per row are loaded before any is used.  For one or
+// two entries the gated MLP and the down projection, the products with the
+// most K per row, split K across the four waves of a block instead (one
+// block per 2 or 4 rows, the waves' sums added in wave order): four times
+// the waves in flight, which the few multiply-adds per loaded weight of a
+// small batch leave room for.  The
 // activations are read from L2 (they are a few KiB and shared by every
 // wave), for small batches in the same round as the weights.  The row sums are reduced across the wave by
 // butterflies in a fixed order, so results do not depend on timing.
@@ -87,10 +92,9 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
                                           const float *__restrict__ x,
                                           const uint16_t *__restrict__ g,
                                           float (&acc)[NW][kRows][B],
-                                          float (&ss)[B]) {
+                                          float (&ss)[B], int cb, int ce) {
   constexpr int U = 4 / NW;  // chunks per row in flight
   const int lane = threadIdx.x & 63;
-  const int nchunk = K >> 3;
 #pragma unroll
   for (int m = 0; m < NW; ++m)
 #pragma unroll
@@ -109,13 +113,13 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
   // The activation chunks (and norm weights) of small batches are loaded
   // with the weight chunks, so one wait covers both round trips.
   constexpr bool XPRE = B <= 2;
-  for (int c0 = 0; c0 < nchunk; c0 += 64 * U) {
+  for (int c0 = cb; c0 < ce; c0 += 64 * U) {
     uint4 wv[NW][kRows][U];
     float4 xp[XPRE ? B : 1][U][2];
     uint4 gp[G && XPRE ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = min(c0 + u * 64 + lane, nchunk - 1);
+      const int c = min(c0 + u * 64 + lane, ce - 1);
 #pragma unroll
       for (int m = 0; m < NW; ++m)
 #pragma unroll
@@ -133,7 +137,7 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 64 + lane;
-      if (c < nchunk) {
+      if (c < ce) {
         float gs[8];
         if constexpr (G) {
           if constexpr (XPRE)
@@ -186,6 +190,55 @@ __device__ __forceinline__ void wave_rows(const uint16_t *const *W, int n0,
   }
 }
 
+// Split K across the block: the four waves share rows n0 .. n0+kRows-1,
+// wave w taking chunks [w n / 4, (w+1) n / 4) of the n = K / 8; the waves'
+// sums are then added in wave order (fixed, so results do not depend on
+// timing).  On return thread t < kRows * B holds row t / B, entry t % B in
+// *v (and v2 for the second matrix) and the full sum of squares in *s2.
+template <int B, int NW, bool G, int kRows>
+__device__ __forceinline__ void block_rows_sk(const uint16_t *const *W,
+                                              int n0, int nrows, int K,
+                                              const float *__restrict__ x,
+                                              const uint16_t *__restrict__ g,
+                                              float *v, float *v2,
+                                              float *s2) {
+  constexpr int NV = NW * kRows * B;
+  __shared__ float red[kWaves][NV + B];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nchunk = K >> 3;
+  float acc[NW][kRows][B], ss[B];
+  wave_rows<B, NW, G, kRows>(W, n0, nrows, K, x, g, acc, ss,
+                             wave * nchunk / kWaves,
+                             (wave + 1) * nchunk / kWaves);
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          red[wave][(m * kRows + r) * B + b] = acc[m][r][b];
+#pragma unroll
+    for (int b = 0; b < B; ++b) red[wave][NV + b] = G ? ss[b] : 0.f;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < kRows * B) {
+    const int b = t % B;
+    float a = red[0][t], a2 = NW > 1 ? red[0][kRows * B + t] : 0.f;
+    float q = red[0][NV + b];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      a += red[w][t];
+      if (NW > 1) a2 += red[w][kRows * B + t];
+      q += red[w][NV + b];
+    }
+    *v = a;
+    *v2 = a2;
+    *s2 = q;
+  }
+}
+
 struct PostArgsK {
   int N, K;
   float eps;
@@ -208,7 +261,8 @@ __global__ __launch_bounds__(kThreads) void gemv_residual_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[1] = {a.w0};
   float acc[1][kRows][B], ss[B];
-  wave_rows<B, 1, false, kRows>(W, n0, nrows, a.K, a.x, nullptr, acc, ss);
+  wave_rows<B, 1, false, kRows>(W, n0, nrows, a.K, a.x, nullptr, acc, ss, 0,
+                                a.K >> 3);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -236,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[2] = {a.w0, a.w1};
   float acc[2][kRows][B], ss[B];
-  wave_rows<B, 2, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  wave_rows<B, 2, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss, 0,
+                               a.K >> 3);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -271,7 +326,8 @@ __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
   const int nrows = min(kRows, a.N - n0);
   const uint16_t *W[1] = {a.w0};
   float acc[1][kRows][B], ss[B];
-  wave_rows<B, 1, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss);
+  wave_rows<B, 1, true, kRows>(W, n0, nrows, a.K, a.x, a.g, acc, ss, 0,
+                               a.K >> 3);
   const int lane = threadIdx.x & 63;
   if (lane < kRows * B) {
     const int r = lane / B, b = lane % B;
@@ -287,6 +343,67 @@ __global__ __launch_bounds__(kThreads) void gemv_norm_kernel(PostArgsK a) {
     if (r < nrows && active(a.skip, b))
       a.y[(size_t)b * a.N + n0 + r] = v / sqrtf(s2 / (float)a.K + a.eps);
   }
+}
+
+// Split-K forms: one block per kRows rows (see block_rows_sk).
+template <int B, int kRows>
+__global__ __launch_bounds__(kThreads) void gemv_residual_sk_kernel(
+    PostArgsK a) {
+  if (!any_active<B>(a.skip)) return;
+  const int n0 = blockIdx.x * kRows;
+  const int nrows = min(kRows, a.N - n0);
+  const uint16_t *W[1] = {a.w0};
+  float v = 0.f, v2 = 0.f, s2 = 0.f;
+  block_rows_sk<B, 1, false, kRows>(W, n0, nrows, a.K, a.x, nullptr, &v, &v2,
+                                    &s2);
+  const int t = threadIdx.x;
+  if (t < kRows * B) {
+    const int r = t / B, b = t % B;
+    if (r < nrows && active(a.skip, b)) {
+      const size_t i = (size_t)b * a.N + n0 + r;
+      a.y[i] = a.base[i] + v;
+    }
+  }
+}
+
+template <int B, int kRows>
+__global__ __launch_bounds__(kThreads) void gate_up_sk_kernel(PostArgsK a) {
+  if (!any_active<B>(a.skip)) return;
+  const int n0 = blockIdx.x * kRows;
+  const int nrows = min(kRows, a.N - n0);
+  const uint16_t *W[2] = {a.w0, a.w1};
+  float gv = 0.f, uv = 0.f, s2 = 0.f;
+  block_rows_sk<B, 2, true, kRows>(W, n0, nrows, a.K, a.x, a.g, &gv, &uv,
+                                   &s2);
+  const int t = threadIdx.x;
+  if (t < kRows * B) {
+    const int r = t / B, b = t % B;
+    if (r < nrows && active(a.skip, b)) {
+      const float rn = 1.f / sqrtf(s2 / (float)a.K + a.eps);
+      gv *= rn;
+      uv *= rn;
+      a.y[(size_t)b * a.N + n0 + r] = gv / (1.f + expf(-gv)) * uv;
+    }
+  }
+}
+
+template <int B, int R>
+struct ResidualSK {
+  static const void *ptr() {
+    return (const void *)gemv_residual_sk_kernel<B, R>;
+  }
+};
+template <int B, int R>
+struct GateUpSK {
+  static const void *ptr() { return (const void *)gate_up_sk_kernel<B, R>; }
+};
+
+// Split-K launch with R rows per block.
+template <template <int, int> class K, int B, int R>
+hipError_t launch_sk(int n_rows, hipStream_t s, PostArgsK a) {
+  const dim3 grid((n_rows + R - 1) / R), block(kThreads);
+  void *argv[1] = {&a};
+  return hipLaunchKernel(K<B, R>::ptr(), grid, block, argv, 0, s);
 }
 
 // Rows per wave for N rows: of 2, 4 and 1 (two rows first for one or two
@@ -361,7 +478,10 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.g = p.norm_mlp;
   a.x = p.h_out;
   a.y = p.m;
-  e = launch_k<GateUpK, B>(a.N, s, a);
+  if constexpr (B <= 2)
+    e = launch_sk<GateUpSK, B, 2>(a.N, s, a);
+  else
+    e = launch_k<GateUpK, B>(a.N, s, a);
   if (e != hipSuccess) return e;
   // h2 = h1 + W_down m, in place
   a = PostArgsK{};
@@ -373,7 +493,10 @@ hipError_t post_b(const PostShape &sh, const PostPtrs &p, hipStream_t s) {
   a.x = p.m;
   a.base = p.h_out;
   a.y = p.h_out;
-  e = launch_k<ResidualK, B>(a.N, s, a);
+  if constexpr (B <= 2)
+    e = launch_sk<ResidualSK, B, 4>(a.N, s, a);
+  else
+    e = launch_k<ResidualK, B>(a.N, s, a);
   if (e != hipSuccess) return e;
   // qkv = W_qkv (rmsnorm(h2) * g_attn)
   a = PostArgsK{};
