@@ -336,9 +336,11 @@ alspec_status alspec_verify(alspec_handle *h, const alspec_params *p,
                             void *stream) {
   if (!h || !p || !o_approx || !o_exact || !ratio || !commit)
     return ALSPEC_ERR_INVALID_ARG;
+  alspec_status st = check_outputs(o_approx, o_exact, o_committed);
+  if (st != ALSPEC_OK) return st;
   alspec::PlanArgs pa;
   alspec::Workspace wl;
-  alspec_status st = alspec::make_plan(p, &pa, &wl);
+  st = alspec::make_plan(p, &pa, &wl);
   if (st != ALSPEC_OK) return st;
   return hip_status(alspec::launch_verify(pa, o_approx, o_exact, ratio, commit,
                                           o_committed, p->lambda,

@@ -1186,35 +1186,84 @@ __global__ __launch_bounds__(kThreads) void lse_middle_kernel(
                             lse_exact);
 }
 
+// Standalone verify, one block per entry: num and den over the entry's
+// Hq * D outputs, read 16 bytes at a time with a thread's loads all in
+// flight, summed per wave in a fixed butterfly order and then in wave
+// order.  Entries of up to kVerifyRegs * 4 * kThreads floats stay in
+// registers, and the committed output is written from them.
+constexpr int kVerifyRegs = 8;
 __global__ __launch_bounds__(kThreads) void verify_kernel(
     int n_per_entry, const float *__restrict__ o_approx,
     const float *__restrict__ o_exact, float *__restrict__ ratio,
     uint8_t *__restrict__ commit, float *__restrict__ o_committed,
     float lambda) {
-  __shared__ float s_red[kWaves];
+  __shared__ float s_n[kWaves], s_d[kWaves];
   __shared__ int s_commit;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, t = threadIdx.x;
   const size_t base = (size_t)b * n_per_entry;
+  const float4 *a4 = (const float4 *)(o_approx + base);
+  const float4 *e4 = (const float4 *)(o_exact + base);
+  const int n4 = n_per_entry >> 2;
+  float4 av[kVerifyRegs], ev[kVerifyRegs];
   float num = 0.f, den = 0.f;
-  for (int i = threadIdx.x; i < n_per_entry; i += kThreads) {
-    const float e = o_exact[base + i];
-    const float diff = o_approx[base + i] - e;
-    num += diff * diff;
-    den += e * e;
+  for (int c0 = 0; c0 < n4; c0 += kVerifyRegs * kThreads) {
+#pragma unroll
+    for (int k = 0; k < kVerifyRegs; ++k) {
+      const int i = c0 + k * kThreads + t;
+      if (i < n4) {
+        av[k] = a4[i];
+        ev[k] = e4[i];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kVerifyRegs; ++k) {
+      if (c0 + k * kThreads + t < n4) {
+        const float4 e = ev[k], a = av[k];
+        const float dx = a.x - e.x, dy = a.y - e.y, dz = a.z - e.z,
+                    dw = a.w - e.w;
+        num += dx * dx;
+        num += dy * dy;
+        num += dz * dz;
+        num += dw * dw;
+        den += e.x * e.x;
+        den += e.y * e.y;
+        den += e.z * e.z;
+        den += e.w * e.w;
+      }
+    }
   }
-  num = block_sum(num, s_red);
-  den = block_sum(den, s_red);
-  if (threadIdx.x == 0) {
-    const float rt = ratio_of(num, den);
+  num = group_sum<64>(num);
+  den = group_sum<64>(den);
+  if ((t & 63) == 0) {
+    s_n[t >> 6] = num;
+    s_d[t >> 6] = den;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float tn = s_n[0], td = s_d[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      tn += s_n[w];
+      td += s_d[w];
+    }
+    const float rt = ratio_of(tn, td);
     ratio[b] = rt;
     s_commit = rt <= lambda ? 1 : 0;
     commit[b] = (uint8_t)s_commit;
   }
   __syncthreads();
   if (o_committed) {
-    const float *src = s_commit ? o_approx : o_exact;
-    for (int i = threadIdx.x; i < n_per_entry; i += kThreads)
-      o_committed[base + i] = src[base + i];
+    float4 *o4 = (float4 *)(o_committed + base);
+    if (n4 <= kVerifyRegs * kThreads) {
+#pragma unroll
+      for (int k = 0; k < kVerifyRegs; ++k) {
+        const int i = k * kThreads + t;
+        if (i < n4) o4[i] = s_commit ? av[k] : ev[k];
+      }
+    } else {
+      const float4 *src = s_commit ? a4 : e4;
+      for (int i = t; i < n4; i += kThreads) o4[i] = src[i];
+    }
   }
 }
 

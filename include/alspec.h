@@ -171,8 +171,9 @@ alspec_status alspec_create(int device, alspec_handle **out);
 alspec_status alspec_destroy(alspec_handle *h);
 
 /*
- * Attention-sink approximation ("a cheap attention-sink approximation",
- * atlas.scime.ai summary, Approach): softmax attention of each query over
+ * Attention-sink approximation (the cheap speculative attention of
+ * "Attention-Level Speculation", atlas.scime.ai research-map page, summary
+ * and Approach): softmax attention of each query over
  * the sink and window tokens only, renormalised over that set.  Writes
  * o_approx [B][Hq][D] and, if non-NULL, lse_approx [B][Hq].  Also leaves in
  * `ws` the per-split states of the sink and window tokens and their merged
@@ -211,9 +212,10 @@ alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
                                  void *stream);
 
 /*
- * Relative L2 verification ("verify with a relative L2 threshold to commit
- * or discard", atlas.scime.ai summary, Approach): per batch entry b over
- * its Hq*D outputs, ratio = ||o_approx - o_exact||_2 / ||o_exact||_2
+ * Relative L2 verification (the check that decides commit or discard in
+ * "Attention-Level Speculation", atlas.scime.ai research-map page, summary
+ * and Approach): per batch entry b over its Hq*D outputs (16-byte aligned,
+ * like o_committed), ratio = ||o_approx - o_exact||_2 / ||o_exact||_2
  * (0 if both norms are 0, +inf if only the exact norm is 0, NaN if any
  * input is NaN) and commit = (ratio <= lambda).  If o_committed is non-NULL
  * it receives o_approx for committed entries and o_exact otherwise.
@@ -298,9 +300,10 @@ typedef struct {
 
 /*
  * The fused step for a chain of n_layers layers of one decode step, on one
- * stream, layer-pipelined: the speculative order ("run the post-attention
- * ops speculatively ... while exact attention is computed",
- * atlas.scime.ai summary, Approach), with layer l+1's query taken to be
+ * stream, layer-pipelined: the speculative order of "Attention-Level
+ * Speculation" (atlas.scime.ai research-map page, summary and Approach:
+ * downstream work starts on the approximation while exact attention is
+ * still running), with layer l+1's query taken to be
  * available once layer l's approximation is.  Launch 0 computes layer 0's
  * approximation; launch j (j = 0..n-1) computes, in disjoint block ranges
  * of one grid, layer j's middle splits, layer j+1's approximation and
