@@ -273,6 +273,21 @@ def test_layers_chain_validation_before_gpu_work():
     assert f(fake_h, ctypes.byref(p), 4, arr, None) == 1
 
 
+def test_verify_rejects_misaligned_outputs_before_gpu_work():
+    """alspec_verify reads and writes its [B][Hq][D] arrays 16 bytes at a
+    time: a misaligned o_approx, o_exact or o_committed is rejected before
+    any HIP call (no GPU needed)."""
+    p = P()
+    f = _binding._verify
+    fake_h = ctypes.c_void_p(0x1000)
+    a = 1 << 40                           # aligned stand-in addresses
+    assert f(fake_h, ctypes.byref(p), a + 4, a, a, a, a, None) == 1
+    assert f(fake_h, ctypes.byref(p), a, a + 8, a, a, a, None) == 1
+    assert f(fake_h, ctypes.byref(p), a, a, a, a, a + 12, None) == 1
+    assert f(None, ctypes.byref(p), a, a, a, a, a, None) == 1
+    assert f(fake_h, ctypes.byref(p), None, a, a, a, a, None) == 1
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(batch=9), 2), (dict(attn_dim=12), 1),
     (dict(hidden=4), 1), (dict(ffn=1001), 1), (dict(qkv_dim=0), 1),
