@@ -89,12 +89,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "2c371cce95c560182d5a32bde2a79a4b"
-                     "319d744a5eadc4ce295e990688aeb588",
+           "sha256": "38fb8406a8c828c076bd065dc17f46a9"
+                     "c439db7019b59ccba33ba31aa933e5d0",
            # (fetch, write) per launch; the chain kernel's in its steady
            # state (all three block ranges)
-           "bytes": {"chain": (262824.0 * 1024 * 2.0, 735.9 * 1024 * 1.0),
-                     "partials_middle": (258173.7 * 1024 * 2.0,
+           "bytes": {"chain": (262811.3 * 1024 * 2.0, 735.9 * 1024 * 1.0),
+                     "partials_middle": (258174.2 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
