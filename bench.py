@@ -151,7 +151,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (world size "
               f"{world}) is not supported: this path has no multi-GPU "
-              "sharding (see DESIGN.md for how it would shard).",
+              "sharding: every figure is for one GPU's full share.",
               file=sys.stderr)
         sys.exit(2)
 
