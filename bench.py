@@ -905,7 +905,20 @@ def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
                       "of the same workload: whole layers (32 heads, context "
                       "131072), double precision, about "
                       f"{args.cpu_seconds:.0f} s of oracle time",
-            "seconds": secs, "sample_flags_agree": f"{agree}/{n}"}
+            "seconds": secs, "sample_flags_agree": f"{agree}/{n}",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
