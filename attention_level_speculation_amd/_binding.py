@@ -166,8 +166,8 @@ def workspace_size(p):
 
 def plan_splits(p, b, layers=False):
     """[(kind, begin, end)] of batch entry b (kind 0 sink, 1 window, 2
-    middle), plus the (middle, window) split lengths; layers=True gives the
-    plan of spec_decode_layers."""
+    middle), plus the (middle, window) split lengths; layers=True asks for
+    the plan of spec_decode_layers by name (the same plan)."""
     fn, name = ((_plan_splits_layers, "alspec_plan_splits_layers") if layers
                 else (_plan_splits, "alspec_plan_splits"))
     cnt = _i32(0)

@@ -154,18 +154,16 @@ alspec_status alspec_workspace_size(const alspec_params *p, size_t *bytes) {
   return ALSPEC_OK;
 }
 
-namespace {
-
-alspec_status plan_splits(alspec::PlanFor use, const alspec_params *p,
-                          int32_t b, int32_t *kind, int32_t *begin,
-                          int32_t *end, int32_t cap, int32_t *count,
-                          int32_t *split_tokens,
-                          int32_t *window_split_tokens) {
+alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
+                                 int32_t *kind, int32_t *begin, int32_t *end,
+                                 int32_t cap, int32_t *count,
+                                 int32_t *split_tokens,
+                                 int32_t *window_split_tokens) {
   if (!p || !count || cap < 0 || (cap > 0 && (!kind || !begin || !end)))
     return ALSPEC_ERR_INVALID_ARG;
   alspec::PlanArgs pa;
   alspec::Workspace wl;
-  alspec_status st = alspec::make_plan(p, &pa, &wl, use);
+  alspec_status st = alspec::make_plan(p, &pa, &wl);
   if (st != ALSPEC_OK) return st;
   if (b < 0 || b >= pa.B) return ALSPEC_ERR_INVALID_ARG;
   int n = 0;
@@ -192,24 +190,13 @@ alspec_status plan_splits(alspec::PlanFor use, const alspec_params *p,
   return ALSPEC_OK;
 }
 
-}  // namespace
-
-alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
-                                 int32_t *kind, int32_t *begin, int32_t *end,
-                                 int32_t cap, int32_t *count,
-                                 int32_t *split_tokens,
-                                 int32_t *window_split_tokens) {
-  return plan_splits(alspec::kPlanStep, p, b, kind, begin, end, cap, count,
-                     split_tokens, window_split_tokens);
-}
-
 alspec_status alspec_plan_splits_layers(const alspec_params *p, int32_t b,
                                         int32_t *kind, int32_t *begin,
                                         int32_t *end, int32_t cap,
                                         int32_t *count, int32_t *split_tokens,
                                         int32_t *window_split_tokens) {
-  return plan_splits(alspec::kPlanLayers, p, b, kind, begin, end, cap, count,
-                     split_tokens, window_split_tokens);
+  return alspec_plan_splits(p, b, kind, begin, end, cap, count, split_tokens,
+                            window_split_tokens);
 }
 
 alspec_status alspec_create(int device, alspec_handle **out) {
@@ -520,7 +507,7 @@ alspec_status alspec_spec_decode_layers(alspec_handle *h,
   if (!h || !p || !layers || n_layers < 1) return ALSPEC_ERR_INVALID_ARG;
   alspec::PlanArgs pa;
   alspec::Workspace wl;
-  alspec_status st = alspec::make_plan(p, &pa, &wl, alspec::kPlanLayers);
+  alspec_status st = alspec::make_plan(p, &pa, &wl);
   if (st != ALSPEC_OK) return st;
   for (int j = 0; j < n_layers; ++j) {
     const alspec_layer &L = layers[j];
@@ -562,7 +549,8 @@ alspec_status alspec_spec_decode_layers(alspec_handle *h,
     if (j >= 1) ver = chain_layer(j - 1);
     if (failed(alspec::launch_chain(pa, p->kv_dtype, &mid,
                                     j + 1 < n_layers ? &app : nullptr,
-                                    j >= 1 ? &ver : nullptr, sm_log2, s),
+                                    j >= 1 ? &ver : nullptr, j >= 1,
+                                    sm_log2, s),
                "launch_chain"))
       return ALSPEC_ERR_HIP;
   }

@@ -70,12 +70,14 @@ struct ChainLayer {
   Outs o;
 };
 
-// One layer-pipelined launch: middle splits of `mid`, the whole
-// approximation of `app` and the exact merge, verify and commit of `ver`
-// (each may be null) in one grid.
+// One layer-pipelined launch in one grid: the merge of `mid`'s sink and
+// window states (split by an earlier launch) if `merge_mid`, the middle
+// splits of `mid`, the sink and window splits of `app`, and the exact
+// merge, verify and commit of `ver` (each layer may be null).
 hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
                         const ChainLayer *mid, const ChainLayer *app,
-                        const ChainLayer *ver, float sm_log2, hipStream_t s);
+                        const ChainLayer *ver, bool merge_mid, float sm_log2,
+                        hipStream_t s);
 
 // Standalone verify of two output buffers.
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,

@@ -1123,28 +1123,35 @@ __global__ __launch_bounds__(kThreads) void merge_verify_kernel(PlanArgs pa,
   verify_block<D, NH>(pa, w, o, blockIdx.x);
 }
 
-// Layer-pipelined launch: one grid holds three disjoint block ranges, all
+// Layer-pipelined launch: one grid holds four disjoint block ranges, all
 // resident at once (three or four 4-wave blocks fit a CU):
-//   [0, nA)              the whole approximation of layer j+1, one block
-//                        per sink or window split, the last of an (entry,
-//                        kv head) to finish merging the group's states,
-//   [nA, nA + nM)        the middle splits of layer j,
-//   [nA + nM, ...)       merge, verify and commit of layer j-1.
-// Launch order alone then carries every dependency of the speculative
-// chain: layer j+1's approximation follows layer j's (one launch earlier),
-// layer j's middle splits follow the approximation of layer j-1, and layer
-// j-1's verify follows its middle splits and approximation.  The short
-// approximation blocks are dispatched first and are done within the first
-// quarter of the launch.  Giving each group's splits to fewer blocks, in
-// turn, spares the device-scope hand-off but made the launch longer: a
-// block's splits run one after another at the streaming blocks' pace.
+//   [0, nG)              the merge of layer j's sink and window states
+//                        (written by the launch before) into its
+//                        approximate output, one block per (entry, kv
+//                        head); dispatched first,
+//   [nG, nG + nA)        the sink and window splits of layer j+1,
+//   [.., + nM)           the middle splits of layer j,
+//   [.., ...)            merge, verify and commit of layer j-1.
+// Launch order alone then carries every dependency of the chain: a
+// layer's merge follows its splits by one launch, its middle splits need
+// nothing of the approximation, and layer j-1's verify follows its
+// middle splits and merged approximation.  No block of the launch hands
+// data to another, so none takes a device-scope fence: merging each
+// group's splits in the same launch (a release per split block, the last
+// one merging) cost about 4 us of a 95 us launch, because the L2
+// write-backs stall the XCDs' streaming blocks.
 template <class KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void chain_kernel(
-    PlanArgs pa, ChainLayer mid, ChainLayer app, ChainLayer ver, int nM,
-    int nA, float sm_log2) {
+    PlanArgs pa, ChainLayer mid, ChainLayer app, ChainLayer ver, int nG,
+    int nM, int nA, float sm_log2) {
   using E = typename KV::elem;
   const int Hq = pa.Hq;
   int idx = blockIdx.x;
+  if (idx < nG) {
+    approx_merge<D, G>(pa, mid.w, mid.o, idx / pa.Hkv, idx % pa.Hkv);
+    return;
+  }
+  idx -= nG;
   if (idx >= nA + nM) {
     idx -= nA + nM;
     if (pa.NHv == 4)
@@ -1165,11 +1172,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
                             it.t0, it.t1, sm_log2,
                             L.w.part_ml + (size_t)it.slot * Hq + h0,
                             L.w.part_acc + ((size_t)it.slot * Hq + h0) * D);
-  if (!approx) return;
-  const unsigned n = (unsigned)(pa.nsink[it.b] + pa.nwin[it.b]);
-  if (!arrive_last(approx_counter(app.w, it.b, pa.Hkv, it.g), n))
-    return;
-  approx_merge<D, G>(pa, app.w, app.o, it.b, it.g);
 }
 
 // Second stage of the exact output from every split state of the plan:
@@ -1369,30 +1371,31 @@ hipError_t approx_combine_d(const PlanArgs &pa, const WsPtrs &w,
 template <class KV, int D, int G>
 hipError_t chain_kg(const PlanArgs &pa, const ChainLayer *mid,
                     const ChainLayer *app, const ChainLayer *ver,
-                    float sm_log2, hipStream_t s) {
+                    bool merge_mid, float sm_log2, hipStream_t s) {
   const ChainLayer none{};
   const int nV = ver ? pa.B * pa.Hq / pa.NHv : 0;
   const int nA = app ? pa.itemA_pre[pa.B] : 0;
   const int nM = mid ? pa.itemM_pre[pa.B] : 0;
-  if (nV + nA + nM == 0) return hipSuccess;
-  return launch(chain_kernel<KV, D, G>, dim3(nV + nA + nM), dim3(kThreads), s,
-                pa, mid ? *mid : none, app ? *app : none, ver ? *ver : none,
-                nM, nA, sm_log2);
+  const int nG = mid && merge_mid ? pa.B * pa.Hkv : 0;
+  if (nG + nV + nA + nM == 0) return hipSuccess;
+  return launch(chain_kernel<KV, D, G>, dim3(nG + nV + nA + nM),
+                dim3(kThreads), s, pa, mid ? *mid : none, app ? *app : none,
+                ver ? *ver : none, nG, nM, nA, sm_log2);
 }
 
 template <class KV, int D>
 hipError_t chain_g(const PlanArgs &pa, const ChainLayer *mid,
-                   const ChainLayer *app, const ChainLayer *ver, float sm_log2,
-                   hipStream_t s) {
+                   const ChainLayer *app, const ChainLayer *ver, bool mm,
+                   float sm_log2, hipStream_t s) {
   switch (pa.G) {
     case 1:
-      return chain_kg<KV, D, 1>(pa, mid, app, ver, sm_log2, s);
+      return chain_kg<KV, D, 1>(pa, mid, app, ver, mm, sm_log2, s);
     case 2:
-      return chain_kg<KV, D, 2>(pa, mid, app, ver, sm_log2, s);
+      return chain_kg<KV, D, 2>(pa, mid, app, ver, mm, sm_log2, s);
     case 4:
-      return chain_kg<KV, D, 4>(pa, mid, app, ver, sm_log2, s);
+      return chain_kg<KV, D, 4>(pa, mid, app, ver, mm, sm_log2, s);
     case 8:
-      return chain_kg<KV, D, 8>(pa, mid, app, ver, sm_log2, s);
+      return chain_kg<KV, D, 8>(pa, mid, app, ver, mm, sm_log2, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1401,13 +1404,16 @@ hipError_t chain_g(const PlanArgs &pa, const ChainLayer *mid,
 
 hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
                         const ChainLayer *mid, const ChainLayer *app,
-                        const ChainLayer *ver, float sm_log2, hipStream_t s) {
+                        const ChainLayer *ver, bool merge_mid, float sm_log2,
+                        hipStream_t s) {
+  const bool mm = merge_mid;
   if (kv_dtype == ALSPEC_KV_BF16) {
-    if (pa.D == 128) return chain_g<KvBf16, 128>(pa, mid, app, ver, sm_log2, s);
-    return chain_g<KvBf16, 64>(pa, mid, app, ver, sm_log2, s);
+    if (pa.D == 128)
+      return chain_g<KvBf16, 128>(pa, mid, app, ver, mm, sm_log2, s);
+    return chain_g<KvBf16, 64>(pa, mid, app, ver, mm, sm_log2, s);
   }
-  if (pa.D == 128) return chain_g<KvF32, 128>(pa, mid, app, ver, sm_log2, s);
-  return chain_g<KvF32, 64>(pa, mid, app, ver, sm_log2, s);
+  if (pa.D == 128) return chain_g<KvF32, 128>(pa, mid, app, ver, mm, sm_log2, s);
+  return chain_g<KvF32, 64>(pa, mid, app, ver, mm, sm_log2, s);
 }
 
 WsPtrs ws_ptrs(void *ws, const Workspace &wl) {

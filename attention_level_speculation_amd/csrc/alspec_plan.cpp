@@ -20,8 +20,7 @@ int pow2_floor(int x) {
 
 }  // namespace
 
-alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
-                        PlanFor use) {
+alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
   if (!p || !pa || !ws) return ALSPEC_ERR_INVALID_ARG;
   const int B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
   const int D = p->head_dim;
@@ -102,19 +101,18 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
     T = (int)(lo * 64);
   }
   // Window split length: the windows of all (entry, kv head) pairs are cut
-  // into about 128 splits in all for a single step, whose approximation is
-  // on the latency path and runs side by side on half the CUs, and into
-  // about 64 for the layer-pipelined call, whose approximation runs beside
-  // a middle pass.  Every split ends in a device-scope hand-off, and those
-  // queue per XCD, so more splits than that cost more than they save.  A
-  // power of two from 64 to 1024 tokens: a longer split streams for long on
-  // one CU (beside a middle split, in the layer-pipelined launch).
+  // into about 128 splits in all, which run side by side on half the CUs.
+  // In a single step every split ends in a device-scope hand-off to the
+  // merge, and those queue per XCD, so more splits cost more than they
+  // save; the layer-pipelined launch has no hand-off (its merge runs in the
+  // next launch) and was fastest at the same count.  A power of two from 64
+  // to 1024 tokens: a longer split streams for long on one CU.
   int Tw = p->window_split_tokens;
   if (Tw == 0) {
     int pairs = 0;
     for (int b = 0; b < B; ++b)
       if (pa->L[b] > pa->w_begin[b]) pairs += Hkv;
-    const int target = use == kPlanLayers ? 64 : 128;
+    const int target = 128;
     const int pieces = pairs > 0 && pairs < target ? target / pairs : 1;
     Tw = max_win / pieces;
     if (Tw < 64) Tw = 64;

@@ -59,17 +59,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // the workspace size needs no device.
 constexpr int kNominalCUs = 256;
 
-// Which call the plan is for: the automatic window split length differs.
-// A single step has its approximation on the latency path and cuts the
-// windows into about 128 splits in all that run side by side; the
-// layer-pipelined call runs the approximation beside a middle pass, where
-// each split's device-scope hand-off costs throughput, and cuts them into
-// about 64.  The step plan never has fewer slots, so its workspace size
-// serves both.
-enum PlanFor { kPlanStep = 0, kPlanLayers = 1 };
-
-// Validate `p` and fill the plan.  Returns ALSPEC_OK or the status to report.
-alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws,
-                        PlanFor use = kPlanStep);
+// Validate `p` and fill the plan (the same for every entry point).  Returns
+// ALSPEC_OK or the status to report.
+alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws);
 
 }  // namespace alspec

@@ -27,11 +27,12 @@ Schedules (overlap modes of the library):
                 after another on one stream (overlap mode 0), as a graph.
   pipelined_eager -- overlap mode 2 issued call by call without a graph.
   layer_pipelined -- alspec_spec_decode_layers on one stream: launch j runs
-                layer j's exact split-K pass, layer j+1's approximation
-                and layer j-1's merge/verify/commit as disjoint block
-                ranges of one grid; stream order carries the speculative
-                dependencies.  Three workspaces in a ring.  Issued eagerly,
-                and (layer_pipelined_graph) as a graph.
+                the merge of layer j's approximation, layer j's exact
+                split-K pass, layer j+1's sink and window splits and layer
+                j-1's merge/verify/commit as disjoint block ranges of one
+                grid; stream order carries the dependencies.  Three
+                workspaces in a ring.  Issued eagerly, and
+                (layer_pipelined_graph) as a graph.
   exact_only_baseline -- not speculative: exact attention over every split
                 and its merge per layer (alspec_flash_decode_exact with the
                 sink and window splits, alspec_lse_combine), as a graph;
@@ -43,10 +44,9 @@ Schedules (overlap modes of the library):
                 the static approximation on the odd layers, exact attention
                 (as in the exact-only baseline) on the even ones, as a graph.
 The headline value is the throughput of the fastest speculative schedule
-(named in config.schedule).  They compute the same outputs; the
-layer-pipelined ones do so with their own automatic window splits (about
-half as many; config.window_split_tokens_layer_pipelined), so they agree
-with the others up to rounding.  The baselines are reported beside it,
+(named in config.schedule).  They compute the same outputs, bit for bit
+(every schedule takes the same split plan).  The baselines are reported
+beside it,
 with each one's output error against exact attention on the same inputs.
 
 Also reported: KV GB/s of the headline schedule's dominant kernel against
@@ -89,12 +89,12 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "38fb8406a8c828c076bd065dc17f46a9"
-                     "c439db7019b59ccba33ba31aa933e5d0",
+           "sha256": "238379be9b2fc354771fea1027101615"
+                     "d9e2a7007d5bc2414caff6ff6717dc38",
            # (fetch, write) per launch; the chain kernel's in its steady
-           # state (all three block ranges)
-           "bytes": {"chain": (262811.3 * 1024 * 2.0, 735.9 * 1024 * 1.0),
-                     "partials_middle": (258174.2 * 1024 * 2.0,
+           # state (all four block ranges)
+           "bytes": {"chain": (262912.2 * 1024 * 2.0, 862.9 * 1024 * 1.0),
+                     "partials_middle": (258167.6 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0)}}
 
 
@@ -555,8 +555,9 @@ def main():
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                 "traffic": measured_traffic("chain"),
                 "kernel": "chain_kernel<KvBf16,128,4> (steady state: "
-                          "approximation of layer j+1, middle splits of "
-                          "layer j, verify of layer j-1)",
+                          "merge of layer j's approximation, middle splits "
+                          "of layer j, sink and window splits of layer j+1, "
+                          "verify of layer j-1)",
                 "algorithmic_bytes_per_launch": layer_bytes,
                 "launch_us_mean": cus,
                 "launches_timed": reps * nd * (nl - 2),

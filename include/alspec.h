@@ -94,13 +94,10 @@ typedef struct {
                                   longest window over (128 / pairs),
                                   rounded down to a power of two from 64
                                   to 1024 tokens, pairs being the (entry,
-                                  kv head) pairs with a window; for
-                                  alspec_spec_decode_layers over (64 /
-                                  pairs) (its approximation runs beside a
-                                  middle pass, where fewer splits mean
-                                  fewer device-scope hand-offs).  Set it
-                                  to give the layered and single calls the
-                                  same plan, and so the same bits. */
+                                  kv head) pairs with a window.  Every
+                                  entry point takes the same plan, so the
+                                  layered and single calls give the same
+                                  bits. */
   int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
                       2 = pipelined (see alspec_spec_decode) */
 } alspec_params;
@@ -154,9 +151,8 @@ alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
                                  int32_t *split_tokens,
                                  int32_t *window_split_tokens);
 
-/* The same for the plan of alspec_spec_decode_layers, which differs only in
- * the automatic window split length.  Its workspace need never exceeds
- * alspec_workspace_size's. */
+/* The plan of alspec_spec_decode_layers, by name: with the automatic rules
+ * above it is alspec_plan_splits's plan. */
 alspec_status alspec_plan_splits_layers(const alspec_params *p, int32_t b,
                                         int32_t *kind, int32_t *begin,
                                         int32_t *end, int32_t cap,
@@ -303,15 +299,21 @@ typedef struct {
  * stream, layer-pipelined: the speculative order of "Attention-Level
  * Speculation" (atlas.scime.ai research-map page, summary and Approach:
  * downstream work starts on the approximation while exact attention is
- * still running), with layer l+1's query taken to be
- * available once layer l's approximation is.  Launch 0 computes layer 0's
- * approximation; launch j (j = 0..n-1) computes, in disjoint block ranges
- * of one grid, layer j's middle splits, layer j+1's approximation and
- * layer j-1's exact merge, verify and commit; a last launch verifies layer
- * n-1.  Stream order alone carries the dependencies, so successive exact
- * passes run back to back with no event or cross-stream wait between
- * them.  Each layer's outputs equal those of alspec_spec_decode (any
- * mode) on its inputs, bit for bit.  p->overlap is ignored.
+ * still running), for layers whose queries are all given (independent
+ * layers).  Launch 0 computes layer 0's approximation; launch j (j =
+ * 0..n-1) computes, in disjoint block ranges of one grid, the merge of
+ * layer j's sink and window states into its approximate output (for j >=
+ * 1; these blocks are dispatched first), layer j's middle splits, layer
+ * j+1's sink and window splits, and layer j-1's exact merge, verify and
+ * commit; a last launch verifies layer n-1.  So layer j's approximate
+ * output is complete a few microseconds into launch j and its exact
+ * output and verdict in launch j+1.  Stream order alone carries the
+ * dependencies, so successive exact passes run back to back with no
+ * event, cross-stream wait or device-scope hand-off between them.  A
+ * stack whose next query is computed from the approximate output runs
+ * through the single-layer calls instead.  Each layer's outputs equal
+ * those of alspec_spec_decode (any mode) on its inputs, bit for bit.
+ * p->overlap is ignored.
  *
  * `layers` is a host array of n_layers entries (>= 1), each validated as
  * the arguments of alspec_spec_decode.  Entries whose layers are fewer
