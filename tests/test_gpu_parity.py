@@ -460,8 +460,8 @@ def _chain(handle, w, n_layers, n_ws=3, lam=None):
 
 def _single_with_chain_plan(p):
     """Params whose single calls use the plan spec_decode_layers takes for
-    p (its automatic window split is longer), so the two agree bit for
-    bit."""
+    p, set explicitly (the automatic plans are the same), so the two agree
+    bit for bit."""
     q = type(p).from_buffer_copy(p)
     q.window_split_tokens = al.plan_splits(p, 0, layers=True)[1][1]
     assert al.plan_splits(q, 0)[1] == al.plan_splits(p, 0, layers=True)[1]
@@ -512,10 +512,9 @@ def test_layers_chain_matches_single_calls(handle, shape, n_layers):
                                              ("llama70b_128k", 3)])
 def test_layers_chain_full_size(handle, shape, n_layers):
     """The chain at full size with the automatic plan, the configuration
-    the benchmark times (a launch with all three block ranges from the
-    third layer on): every layer against the oracle, and bit for bit
-    against single fused calls on its inputs with the chain's plan (whose
-    automatic window splits are at least as long as a single call's)."""
+    the benchmark times (launches with all four block ranges between the
+    first and the last): every layer against the oracle, and bit for bit
+    against single fused calls on its inputs with the chain's plan."""
     w = {"llama8b_128k": gen.llama8b_128k(needles=4),
          "llama70b_128k": gen.llama70b_128k()}[shape]
     p = al.params_for(w)
