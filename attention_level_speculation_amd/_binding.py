@@ -8,11 +8,19 @@ is no fallback: if the library is not built, importing the package fails.
 import ctypes
 import math
 import os
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+IN_TREE_LIB = os.path.join(HERE, "libalspec.so")
 # ALSPEC_LIB selects another build of the same library (e.g. a variant
-# built with different compile-time options); default: the in-tree build.
-LIB_PATH = os.environ.get("ALSPEC_LIB") or os.path.join(HERE, "libalspec.so")
+# built with different compile-time options) for timing comparisons; the
+# benchmark records the path it loaded.  The test suite always checks the
+# in-tree build: under pytest a different path is refused.
+LIB_PATH = os.environ.get("ALSPEC_LIB") or IN_TREE_LIB
+if "pytest" in sys.modules and (os.path.realpath(LIB_PATH) !=
+                                os.path.realpath(IN_TREE_LIB)):
+    raise ImportError(f"ALSPEC_LIB={LIB_PATH} is not honoured under pytest: "
+                      "the tests check the in-tree library")
 
 KV_F32 = 0
 KV_BF16 = 1
@@ -83,9 +91,6 @@ _workspace_size = _sig("alspec_workspace_size", _PP,
 _plan_splits = _sig("alspec_plan_splits", _PP, _i32, _P, _P, _P, _i32,
                     ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                     ctypes.POINTER(_i32))
-_plan_splits_layers = _sig("alspec_plan_splits_layers", _PP, _i32, _P, _P,
-                           _P, _i32, ctypes.POINTER(_i32),
-                           ctypes.POINTER(_i32), ctypes.POINTER(_i32))
 _create = _sig("alspec_create", ctypes.c_int, ctypes.POINTER(_P))
 _destroy = _sig("alspec_destroy", _P)
 _sink_approx = _sig("alspec_sink_approx", _P, _PP, _P, _P, _P, _P, _P, _P,
@@ -164,23 +169,23 @@ def workspace_size(p):
     return int(n.value)
 
 
-def plan_splits(p, b, layers=False):
+def plan_splits(p, b):
     """[(kind, begin, end)] of batch entry b (kind 0 sink, 1 window, 2
-    middle), plus the (middle, window) split lengths; layers=True asks for
-    the plan of spec_decode_layers by name (the same plan)."""
-    fn, name = ((_plan_splits_layers, "alspec_plan_splits_layers") if layers
-                else (_plan_splits, "alspec_plan_splits"))
+    middle), plus the (middle, window) split lengths.  Every entry point
+    takes this plan."""
+    name = "alspec_plan_splits"
     cnt = _i32(0)
     t = _i32(0)
     tw = _i32(0)
-    _check(fn(ctypes.byref(p), b, None, None, None, 0, ctypes.byref(cnt),
-              ctypes.byref(t), ctypes.byref(tw)), name)
+    _check(_plan_splits(ctypes.byref(p), b, None, None, None, 0,
+                        ctypes.byref(cnt), ctypes.byref(t), ctypes.byref(tw)),
+           name)
     n = cnt.value
     kind = (_i32 * max(1, n))()
     beg = (_i32 * max(1, n))()
     end = (_i32 * max(1, n))()
-    _check(fn(ctypes.byref(p), b, kind, beg, end, n, ctypes.byref(cnt), None,
-              None), name)
+    _check(_plan_splits(ctypes.byref(p), b, kind, beg, end, n,
+                        ctypes.byref(cnt), None, None), name)
     return [(kind[i], beg[i], end[i]) for i in range(n)], (t.value, tw.value)
 
 
@@ -217,6 +222,24 @@ def _ptr(t, dtype, shape, name, allow_none=False):
 def _kv_torch_dtype(p):
     torch = _torch()
     return torch.bfloat16 if p.kv_dtype == KV_BF16 else torch.float32
+
+
+_hip = None
+
+
+def stream_is_capturing(s):
+    """Whether torch stream `s` is recording into a HIP graph (asked of the
+    HIP runtime torch loaded, reached by its soname)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipStreamIsCapturing.argtypes = [_P, ctypes.POINTER(ctypes.c_int)]
+        _hip.hipStreamIsCapturing.restype = ctypes.c_int
+    status = ctypes.c_int(0)
+    err = _hip.hipStreamIsCapturing(_P(s.cuda_stream), ctypes.byref(status))
+    if err != 0:
+        raise RuntimeError(f"hipStreamIsCapturing failed ({err})")
+    return status.value == 1        # hipStreamCaptureStatusActive
 
 
 def _stream(s):

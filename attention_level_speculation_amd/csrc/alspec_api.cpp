@@ -190,15 +190,6 @@ alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
   return ALSPEC_OK;
 }
 
-alspec_status alspec_plan_splits_layers(const alspec_params *p, int32_t b,
-                                        int32_t *kind, int32_t *begin,
-                                        int32_t *end, int32_t cap,
-                                        int32_t *count, int32_t *split_tokens,
-                                        int32_t *window_split_tokens) {
-  return alspec_plan_splits(p, b, kind, begin, end, cap, count, split_tokens,
-                            window_split_tokens);
-}
-
 alspec_status alspec_create(int device, alspec_handle **out) {
   if (!out) return ALSPEC_ERR_INVALID_ARG;
   *out = nullptr;
@@ -302,16 +293,15 @@ alspec_status alspec_flash_decode_exact(alspec_handle *h,
 }
 
 alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
-                                 const void *ws, size_t ws_bytes,
-                                 float *o_exact, float *lse_exact,
-                                 void *stream) {
+                                 void *ws, size_t ws_bytes, float *o_exact,
+                                 float *lse_exact, void *stream) {
   if (!h || !p || !o_exact) return ALSPEC_ERR_INVALID_ARG;
   alspec::PlanArgs pa;
   alspec::Workspace wl;
   alspec_status st = alspec::make_plan(p, &pa, &wl);
   if (st != ALSPEC_OK) return st;
   if ((st = check_ws(ws, ws_bytes, wl)) != ALSPEC_OK) return st;
-  const alspec::WsPtrs w = alspec::ws_ptrs((void *)ws, wl);
+  const alspec::WsPtrs w = alspec::ws_ptrs(ws, wl);
   return hip_status(alspec::launch_lse_combine(pa, w, o_exact, lse_exact,
                                                (hipStream_t)stream),
                     "launch_lse_combine");

@@ -202,7 +202,6 @@ def main():
              "sink": (None, True), "fixsink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
-    Tw_layers = al.plan_splits(P["chain"], 0, layers=True)[1][1]
     n_mid = sum(1 for s in splits if s[0] == 2)
     mid_tokens = sum(e - b for k, b, e in splits if k == 2)
     a_tokens = sum(e - b for k, b, e in splits if k != 2)
@@ -511,12 +510,12 @@ def main():
             "num_kv_heads": w0.Hkv, "head_dim": w0.D, "sink": w0.S,
             "window": w0.W, "lambda": w0.lam, "split_tokens": T,
             "window_split_tokens": Tw,
-            "window_split_tokens_layer_pipelined": Tw_layers,
             "middle_splits_per_head": n_mid,
             "generator": {"a": w0.const.a, "c_s": w0.const.c_s,
                           "tau_s": w0.const.tau_s, "c_n": w0.const.c_n,
                           "tau_n": w0.const.tau_n},
         },
+        "library": _library_record(al.LIB_PATH),
         "hit_rate": hit_rate,
         "hit_rate_by_needles": hits,
         "output_error": quality,
@@ -908,6 +907,18 @@ def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):
                       f"{args.cpu_seconds:.0f} s of oracle time",
             "seconds": secs, "sample_flags_agree": f"{agree}/{n}",
             "cpu_model": _cpu_model()}
+
+
+def _library_record(path):
+    """The HIP library this run loaded: its path (relative to the
+    repository when inside it) and the first 16 hex digits of its
+    sha256."""
+    import hashlib
+    with open(path, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    rel = os.path.relpath(os.path.realpath(path), os.path.realpath(ROOT))
+    return {"path": path if rel.startswith("..") else rel,
+            "sha256_16": digest}
 
 
 def _cpu_model():

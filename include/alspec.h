@@ -151,14 +151,6 @@ alspec_status alspec_plan_splits(const alspec_params *p, int32_t b,
                                  int32_t *split_tokens,
                                  int32_t *window_split_tokens);
 
-/* The plan of alspec_spec_decode_layers, by name: with the automatic rules
- * above it is alspec_plan_splits's plan. */
-alspec_status alspec_plan_splits_layers(const alspec_params *p, int32_t b,
-                                        int32_t *kind, int32_t *begin,
-                                        int32_t *end, int32_t cap,
-                                        int32_t *count, int32_t *split_tokens,
-                                        int32_t *window_split_tokens);
-
 /* Create a handle bound to HIP device `device`: the events the fused call
  * uses for cross-stream ordering, a 16-entry table of workspace events and
  * the pipelined mode's verify stream (default priority).  *out is set on
@@ -197,15 +189,24 @@ alspec_status alspec_flash_decode_exact(alspec_handle *h,
                                         size_t ws_bytes, void *stream);
 
 /*
- * Log-sum-exp combine of every split state of the plan held in `ws`
- * (sink, window and middle splits, all of which must have been written)
- * into exact attention: o_exact [B][Hq][D] and, if non-NULL,
- * lse_exact [B][Hq].
+ * Log-sum-exp combine of split states into exact attention: flash
+ * decoding's merge of per-range softmax states, which the pages name as a
+ * building block ("Attention-Level Speculation", atlas.scime.ai summary,
+ * "Builds on").  Every split state of the plan must be present in `ws`
+ * (sink, window and middle splits: alspec_flash_decode_exact with
+ * include_sink_window = 1, or alspec_sink_approx followed by
+ * alspec_flash_decode_exact with 0).  Writes o_exact [B][Hq][D] and, if
+ * non-NULL, lse_exact [B][Hq].
+ *
+ * `ws` is written as well as read: the call first merges the sink and
+ * window states into the workspace's merged sink+window state (the same
+ * state alspec_sink_approx leaves there, with the same bits), then merges
+ * the middle states onto it.  So the call may not overlap in time with any
+ * other call on the same workspace.
  */
 alspec_status alspec_lse_combine(alspec_handle *h, const alspec_params *p,
-                                 const void *ws, size_t ws_bytes,
-                                 float *o_exact, float *lse_exact,
-                                 void *stream);
+                                 void *ws, size_t ws_bytes, float *o_exact,
+                                 float *lse_exact, void *stream);
 
 /*
  * Relative L2 verification (the check that decides commit or discard in
@@ -379,8 +380,10 @@ typedef struct {
 alspec_status alspec_post_workspace_size(const alspec_post_params *p,
                                          size_t *bytes);
 
-/* The post-attention operators for B entries, four kernel launches on
- * `stream`, in fp32 arithmetic on bf16 weights.
+/* The post-attention operators ("Attention-Level Speculation",
+ * atlas.scime.ai summary, Approach: the work run speculatively on the
+ * approximate output) for B entries, four kernel launches on `stream`, in
+ * fp32 arithmetic on bf16 weights.
  *   o      fp32 [B][attn_dim] attention output (device)
  *   h_in   fp32 [B][hidden] residual stream in (device)
  *   h_out  fp32 [B][hidden] residual stream out (device; may equal h_in)

@@ -81,7 +81,7 @@ def test_random_shape(handle, i):
                                       in enumerate(zip(devs, outs))])
     torch.cuda.synchronize()
     ps = type(p).from_buffer_copy(p)
-    ps.window_split_tokens = al.plan_splits(p, 0, layers=True)[1][1]
+    ps.window_split_tokens = al.plan_splits(p, 0)[1][1]
     for j, d in enumerate(devs):
         got_j = {k_: v_.cpu().numpy() for k_, v_ in outs[j].items()}
         compare(got_j, refs[j], w.kv_dtype, w.lam, f"rand{i}-chain{j}")
