@@ -18,8 +18,9 @@
  * computed as well; the approximation is checked against the exact output
  * with a relative L2 threshold (lambda = 0.10 in the evaluation) and is then
  * committed or discarded ([P1] Summary, Approach, Key results; [P2]
- * abstract).  Correctness was simulated by running both attention paths
- * ([P1] Limitations), which is what this oracle does.
+ * abstract).  The pages' evaluation checked the outcome in simulation,
+ * with the approximate and the exact attention both evaluated ([P1]
+ * Limitations); this oracle likewise computes both.
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
