@@ -10,11 +10,13 @@ operators, alspec_post_attention), enqueued on HIP streams.  Whether a
 layer's replay does any work is decided on the device: the replay kernels
 read the layer's commit flag and end at once where it is set, so the
 sequence of launches is static and the work dynamic.  The two-stream form
-is issued eagerly: its two streams wait on each other in turn, and
+is issued eagerly only: its two streams wait on each other in turn, and
 capturing that into a HIP graph ended in a host segmentation fault inside
-hipStreamEndCapture with the HIP runtime torch loads.  The one-stream form
-(one_stream=True) issues the same work in dependency order on one stream,
-so the whole stack of layers captures into one HIP graph.
+hipStreamEndCapture with the HIP runtime torch loads, so model_step
+refuses it (ValueError, nothing enqueued) while either stream is
+capturing.  The one-stream form (one_stream=True) issues the same work in
+dependency order on one stream, so the whole stack of layers captures
+into one HIP graph.
 
 Per layer l, with q_l the first Hq*D entries of the previous layer's QKV
 projection (one decode token, batch 1):
@@ -75,9 +77,18 @@ def model_step(h, p, pp, q0, layers, ws_attn, ws_post_a, ws_post_b,
     post-attention work on its output, the non-speculative baseline;
     one_stream=True (with speculative) runs the speculative form on
     stream_exact alone, in an order a stream capture can record.  Layer l's
-    query is layers[l-1].qkv_out's query part."""
+    query is layers[l-1].qkv_out's query part.  The two-stream speculative
+    form raises ValueError, before enqueuing anything, if either stream is
+    capturing into a HIP graph."""
     if p.batch != 1 or pp.batch != 1:
         raise ValueError("the chained step takes one decode token (batch 1)")
+    if (speculative and not one_stream and not exact_only and
+            (B_.stream_is_capturing(stream_approx) or
+             B_.stream_is_capturing(stream_exact))):
+        raise ValueError("the two-stream speculative step is not captured "
+                         "(its capture crashed the HIP runtime's "
+                         "hipStreamEndCapture); use one_stream=True under "
+                         "stream capture")
     p0 = B_.Params.from_buffer_copy(p)
     p0.overlap = 0
     sa = stream_approx if speculative else stream_exact
