@@ -67,19 +67,54 @@ def rel_l2(a, b):
     return np.linalg.norm(a - b) / n if n > 0 else np.linalg.norm(a - b)
 
 
+# Worst errors of every compare() call in this process, by label (written
+# out at the end of the session when ALSPEC_MARGINS names a file).
+MARGINS = []
+
+
 def compare(got, ref, kv_dtype, lam, label=""):
     """Assert parity of one call's outputs with the oracle; returns a dict
-    of the worst errors."""
+    of the worst errors.
+
+    For O_exact and O_approx of every batch entry, three bars at the same
+    tolerance tol (1e-5 fp32 KV, 2e-3 bf16 KV):
+      - the entry's relative L2 error over its Hq*D outputs;
+      - every query head's relative L2 error over its D outputs, so that a
+        wrong head cannot hide in the entry's norm;
+      - every element: |got - ref| <= tol * max|ref| over the entry, so that
+        a wrong lane or element cannot either.
+    Then lse within 1e-4 nats, the ratio within 1e-4, flags equal outside
+    the 1e-4 band around lambda, and the committed output equal, bit for
+    bit, to the output its flag selects."""
     tol = TOL[kv_dtype]
     B = ref["ratio"].shape[0]
-    worst = {"o_exact": 0.0, "o_approx": 0.0, "ratio": 0.0, "lse": 0.0}
+    worst = {"o_exact": 0.0, "o_approx": 0.0, "o_exact_head": 0.0,
+             "o_approx_head": 0.0, "o_exact_elem": 0.0, "o_approx_elem": 0.0,
+             "ratio": 0.0, "lse": 0.0}
     for b in range(B):
         if not np.isfinite(ref["ratio"][b]):
             continue
         for key in ("o_exact", "o_approx"):
-            e = rel_l2(got[key][b], ref[key][b])
+            g = np.asarray(got[key][b], np.float64)
+            r = np.asarray(ref[key][b], np.float64)
+            e = rel_l2(g, r)
             worst[key] = max(worst[key], e)
             assert e <= tol, f"{label} entry {b} {key} rel err {e:.3g} > {tol}"
+            for h in range(r.shape[0]):
+                eh = rel_l2(g[h], r[h])
+                worst[key + "_head"] = max(worst[key + "_head"], eh)
+                assert eh <= tol, (f"{label} entry {b} head {h} {key} rel "
+                                   f"err {eh:.3g} > {tol}")
+            scale = np.abs(r).max()
+            de = np.abs(g - r).max() / scale if scale > 0 else \
+                np.abs(g - r).max()
+            worst[key + "_elem"] = max(worst[key + "_elem"], de)
+            if de > tol:
+                h, d = np.unravel_index(np.argmax(np.abs(g - r)), r.shape)
+                raise AssertionError(
+                    f"{label} entry {b} {key}[{h}][{d}] = {g[h, d]!r}, "
+                    f"oracle {r[h, d]!r}: error {de:.3g} of the entry's "
+                    f"largest output > {tol}")
         for gk, rk in (("lse_exact", "lse_exact"), ("lse_approx", "lse_approx")):
             d = np.abs(got[gk][b] - ref[rk][b]).max()
             worst["lse"] = max(worst["lse"], d)
@@ -94,6 +129,8 @@ def compare(got, ref, kv_dtype, lam, label=""):
         sel = got["o_approx"][b] if got["commit"][b] else got["o_exact"][b]
         assert np.array_equal(got["o_committed"][b], sel), \
             f"{label} entry {b} committed output"
+    MARGINS.append({"label": label, "kv_dtype": kv_dtype, "tol": tol,
+                    **{k_: float(v_) for k_, v_ in worst.items()}})
     return worst
 
 

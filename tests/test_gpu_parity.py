@@ -175,6 +175,64 @@ def test_edge_shapes(handle, case):
     compare(stand, ref, dt, w.lam, name + "-standalone")
 
 
+# Shapes that take the kernels' less common branches (plans computed on the
+# host): the sink and window merge over more states than one memory round
+# holds (a max pass, then rounds), the exact merge likewise over many middle
+# states, and the standalone verify over more outputs per entry than its
+# registers hold.
+BRANCHES = [
+    # name, B, Hq, Hkv, D, lens, dtype, S, W, split, wsplit
+    # 70B shape at batch 1, automatic plan: 17 sink and window states
+    # against 9 per round of an 8-head merge
+    ("approx_rounds_g8_auto", 1, 64, 8, 128, [20000], "bf16", 4, 2048, 0, 0),
+    # 33 states against 9 (G = 8) and against 18 (G = 4)
+    ("approx_rounds_g8_w64", 1, 64, 8, 128, [20000], "bf16", 4, 2048, 0, 64),
+    ("approx_rounds_g4_w64", 1, 32, 8, 128, [20000], "bf16", 4, 2048, 0, 64),
+    # about 300 middle states per head against 64 per round, both dtypes
+    ("exact_rounds_f32", 1, 8, 2, 128, [20000], "f32", 4, 1024, 64, 0),
+    ("exact_rounds_bf16", 1, 8, 2, 128, [20000], "bf16", 4, 1024, 64, 0),
+    ("exact_rounds_d64_f32", 1, 8, 2, 64, [20000], "f32", 4, 1024, 64, 0),
+    # automatic plan: 75 middle states against 64
+    ("exact_rounds_auto", 1, 8, 2, 128, [20000], "bf16", 4, 1024, 0, 0),
+    # 16384 outputs per entry: the standalone verify's streaming form
+    ("verify_large_entry", 2, 128, 16, 128, [700, 1500], "bf16", 4, 128, 0,
+     0),
+]
+
+
+@pytest.mark.parametrize("case", BRANCHES, ids=[c[0] for c in BRANCHES])
+def test_merge_and_verify_branches(handle, case):
+    """Each branch shape through the fused call (two streams), the
+    standalone calls (with the sink and window states from the
+    approximation, and with every split recomputed), and a three-layer
+    chain: every layer against the oracle, and the chain bit for bit
+    against single fused calls with its plan."""
+    name, B, Hq, Hkv, D, lens, dt, S, W, split, wsplit = case
+    w = _mk(name, B, Hq, Hkv, D, lens, dt, S, W)
+    q, k, v, ref, got, p, dev = _case(handle, w, split_tokens=split,
+                                      window_split_tokens=wsplit)
+    stand = run_standalone(al, handle, p, *dev)
+    compare(stand, ref, dt, w.lam, name + "-standalone")
+    allsp = run_standalone(al, handle, p, *dev, include_sink_window=True)
+    compare(allsp, ref, dt, w.lam, name + "-standalone-all-splits")
+    assert np.array_equal(allsp["o_exact"], got["o_exact"])
+    assert np.array_equal(stand["o_approx"], got["o_approx"])
+    devs = [dev] + [to_device(*gen.layer_inputs(w, l)) for l in (1, 2)]
+    refs = [ref] + [oracle.spec_decode(*gen.layer_inputs(w, l), w.seq_lens,
+                                       w.S, w.W, w.lam) for l in (1, 2)]
+    wss = [al.alloc_workspace(p) for _ in range(3)]
+    outs = [al.alloc_outputs(p) for _ in range(3)]
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j]) for j, (d, o) in
+                                      enumerate(zip(devs, outs))])
+    torch.cuda.synchronize()
+    for j, d in enumerate(devs):
+        got_j = {k_: v_.cpu().numpy() for k_, v_ in outs[j].items()}
+        compare(got_j, refs[j], dt, w.lam, f"{name}-chain{j}")
+        single = run_fused(al, handle, p, *d)
+        for key in single:
+            assert np.array_equal(got_j[key], single[key]), (j, key)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_full_cover_gives_ratio_exactly_zero(handle, dt):
     """S + W >= L: the middle is empty, the exact merge repeats the
@@ -460,11 +518,11 @@ def _chain(handle, w, n_layers, n_ws=3, lam=None):
 
 def _single_with_chain_plan(p):
     """Params whose single calls use the plan spec_decode_layers takes for
-    p, set explicitly (the automatic plans are the same), so the two agree
-    bit for bit."""
+    p (every entry point takes one plan), with the window split set
+    explicitly, so the two agree bit for bit."""
     q = type(p).from_buffer_copy(p)
-    q.window_split_tokens = al.plan_splits(p, 0, layers=True)[1][1]
-    assert al.plan_splits(q, 0)[1] == al.plan_splits(p, 0, layers=True)[1]
+    q.window_split_tokens = al.plan_splits(p, 0)[1][1]
+    assert al.plan_splits(q, 0)[1] == al.plan_splits(p, 0)[1]
     return q
 
 
