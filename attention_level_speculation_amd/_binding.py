@@ -103,6 +103,10 @@ _verify = _sig("alspec_verify", _P, _PP, _P, _P, _P, _P, _P, _P)
 _order_after_verify = _sig("alspec_order_after_verify", _P, _P)
 _spec_decode_layers = _sig("alspec_spec_decode_layers", _P, _PP, _i32,
                            ctypes.POINTER(Layer), _P)
+_spec_decode_noalloc = _sig("alspec_spec_decode_noalloc", _P, _PP, _P, _P,
+                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            ctypes.POINTER(Events))
+NOALLOC_SCRATCH_BYTES = 16 << 20
 _spec_decode = _sig("alspec_spec_decode", _P, _PP, _P, _P, _P, _P, _P, _P,
                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
                     ctypes.POINTER(Events))
@@ -390,6 +394,30 @@ def spec_decode(h, p, q, k, v, out, ws, stream_approx=None,
              "o_committed", True),
         wp, wn, sa, se, ctypes.byref(ev) if ev is not None else None),
         "alspec_spec_decode")
+
+
+def spec_decode_noalloc(h, p, q, k, v, out, stream_approx=None,
+                        stream_exact=None):
+    """The fused step with the library's static scratch as its workspace
+    (alspec_spec_decode_noalloc): no workspace argument, nothing
+    allocated.  Calls that overlap in time on one GPU race."""
+    torch = _torch()
+    qp, kp, vp = _qkv(p, q, k, v)
+    B, Hq, D = p.batch, p.num_q_heads, p.head_dim
+    sa = _stream(stream_approx)
+    se = _stream(stream_exact if stream_exact is not None else stream_approx)
+    _check(_spec_decode_noalloc(
+        h.ptr, ctypes.byref(p), qp, kp, vp,
+        _ptr(out["o_approx"], torch.float32, (B, Hq, D), "o_approx"),
+        _ptr(out.get("lse_approx"), torch.float32, (B, Hq), "lse_approx",
+             True),
+        _ptr(out["o_exact"], torch.float32, (B, Hq, D), "o_exact"),
+        _ptr(out.get("lse_exact"), torch.float32, (B, Hq), "lse_exact", True),
+        _ptr(out["ratio"], torch.float32, (B,), "ratio"),
+        _ptr(out["commit"], torch.uint8, (B,), "commit"),
+        _ptr(out.get("o_committed"), torch.float32, (B, Hq, D),
+             "o_committed", True), sa, se, None),
+        "alspec_spec_decode_noalloc")
 
 
 def layers_struct(p, layers):

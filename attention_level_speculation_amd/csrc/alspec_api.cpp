@@ -10,6 +10,10 @@
 #include "alspec.h"
 #include "alspec_kernels.h"
 #include "alspec_plan.h"
+#include "alspec_scratch.h"
+
+static_assert(ALSPEC_NOALLOC_SCRATCH_BYTES == alspec::kScratchBytes,
+              "the header states the static scratch's size");
 
 // Fused calls remember, per workspace, the event that follows the last
 // verify reading it, so that a later call on that workspace in another
@@ -50,6 +54,7 @@ struct alspec_handle {
   hipEvent_t ev_verify;  // verify stream tail (alspec_order_after_verify)
   WsEntry ws_table[kWsTable];
   uint64_t tick;
+  void *scratch;  // this device's static scratch (allocation-free call)
 };
 
 namespace {
@@ -220,6 +225,10 @@ alspec_status alspec_create(int device, alspec_handle **out) {
               !failed(hipStreamCreateWithFlags(&h->sv, hipStreamNonBlocking),
                       "hipStreamCreateWithFlags");
     for (int i = 0; ok && i < kWsTable; ++i) ok = event(&h->ws_table[i].ev);
+    // the allocation-free call's scratch on this device (set up once per
+    // device and process, with the device current)
+    ok = ok && !failed(alspec::scratch_setup(device, h->sv, &h->scratch),
+                       "scratch_setup");
     if (!ok) {
       alspec_destroy(h);
       h = nullptr;
@@ -487,6 +496,35 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
     return ALSPEC_ERR_HIP;
   if ((st = verify(se)) != ALSPEC_OK) return st;
   return done_ws(se);
+}
+
+alspec_status alspec_spec_decode_noalloc(
+    alspec_handle *h, const alspec_params *p, const float *q, const void *k,
+    const void *v, float *o_approx, float *lse_approx, float *o_exact,
+    float *lse_exact, float *ratio, uint8_t *commit, float *o_committed,
+    void *stream_approx, void *stream_exact, const alspec_events *ev) {
+  if (!h) return ALSPEC_ERR_INVALID_ARG;
+  if (!h->scratch) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "no static scratch on device %d (devices 0..%d have one)",
+             h->device, alspec::kScratchMaxDevices - 1);
+    return ALSPEC_ERR_UNSUPPORTED;
+  }
+  size_t need = 0;
+  alspec_status st = alspec_workspace_size(p, &need);
+  if (st != ALSPEC_OK) return st;
+  if (need > alspec::kScratchBytes) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "workspace of %zu bytes exceeds the static scratch of %zu bytes",
+             need, alspec::kScratchBytes);
+    return ALSPEC_ERR_WORKSPACE;
+  }
+  // The scratch is passed as the fused call's workspace: the same kernels,
+  // the same bits, and the same workspace ordering of uncaptured calls.
+  return alspec_spec_decode(h, p, q, k, v, o_approx, lse_approx, o_exact,
+                            lse_exact, ratio, commit, o_committed, h->scratch,
+                            alspec::kScratchBytes, stream_approx,
+                            stream_exact, ev);
 }
 
 alspec_status alspec_spec_decode_layers(alspec_handle *h,

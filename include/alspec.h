@@ -131,9 +131,10 @@ const char *alspec_status_string(alspec_status s);
 int32_t alspec_version(void);
 
 /* Text naming the HIP call and HIP error behind the most recent
- * ALSPEC_ERR_HIP returned on the calling thread ("" if none yet).  The
- * string is thread-local and stays valid until the thread's next failing
- * call. */
+ * ALSPEC_ERR_HIP returned on the calling thread, or the sizes behind an
+ * ALSPEC_ERR_WORKSPACE of alspec_spec_decode_noalloc ("" if none yet).
+ * The string is thread-local and stays valid until the thread's next
+ * failing call. */
 const char *alspec_last_error(void);
 
 /* Bytes of workspace the compute calls need for these parameters.  Pure
@@ -281,6 +282,36 @@ alspec_status alspec_spec_decode(alspec_handle *h, const alspec_params *p,
                                  float *o_committed, void *ws,
                                  size_t ws_bytes, void *stream_approx,
                                  void *stream_exact, const alspec_events *ev);
+
+/* Size of the static scratch of alspec_spec_decode_noalloc, per GPU. */
+#define ALSPEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * For callers that cannot allocate device memory (work recorded under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * alspec_spec_decode with no workspace argument.  The workspace is a
+ * static device array of ALSPEC_NOALLOC_SCRATCH_BYTES (16 MiB) inside the
+ * library, one per GPU, set up by alspec_create (its device address looked
+ * up and its counters cleared, once per device and process) and held until
+ * the process ends.  The call allocates nothing; the caller still passes
+ * every input and output, as to alspec_spec_decode, whose kernels and bits
+ * it shares.
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls whose work overlaps in time on the same GPU race,
+ * from any handle or thread.  Uncaptured calls through one handle are
+ * ordered by its workspace table as alspec_spec_decode's are; calls through
+ * different handles, and captured calls, are ordered by the caller.
+ * Parameters whose workspace (alspec_workspace_size) exceeds the array
+ * return ALSPEC_ERR_WORKSPACE with nothing enqueued, and alspec_last_error
+ * then names both sizes.  A handle on a device past index 63 has no array
+ * (ALSPEC_ERR_UNSUPPORTED).
+ */
+alspec_status alspec_spec_decode_noalloc(
+    alspec_handle *h, const alspec_params *p, const float *q, const void *k,
+    const void *v, float *o_approx, float *lse_approx, float *o_exact,
+    float *lse_exact, float *ratio, uint8_t *commit, float *o_committed,
+    void *stream_approx, void *stream_exact, const alspec_events *ev);
 
 /* One layer's buffers for alspec_spec_decode_layers: as the arguments of
  * alspec_spec_decode (device pointers; lse_approx, lse_exact and
