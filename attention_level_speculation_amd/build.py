@@ -10,10 +10,13 @@ SOURCES = ["alspec_kernels.hip", "alspec_post.hip", "alspec_scratch.hip",
            "alspec_api.cpp", "alspec_plan.cpp"]
 
 # Packed fp32 instructions stay off (the compiler would otherwise form them
-# from plain float code).
+# from plain float code).  The leading scalar kernel arguments (up to 10) are
+# preloaded into scalar registers at wave launch where the firmware supports
+# it (the code keeps a prologue that loads them otherwise).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Wall", "-Wno-unused-function",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-kernarg-preload-count=10"]
 
 
 def build(verbose: bool = False, extra=()) -> str:
