@@ -135,6 +135,11 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--configs", default="c2,c4,c5",
+                    help="other configurations timed as layer-pipelined "
+                         "chains after the headline: c2 (8B shape at 32K), "
+                         "c4 (8 users, ragged 64K-128K), c5 (70B shape, 4 "
+                         "users at 128K, 80 layers); 'none' to skip")
     ap.add_argument("--model-steps", type=int, default=10,
                     help="timed tokens of the chained decode step with "
                          "post-attention work (0: skip)")
@@ -524,6 +529,33 @@ def main():
     }
     out["step_hbm_frac"] = out["step_kv_GBps"] / HBM_PEAK_GBPS
     out.update(res)
+    # ---- the pages' measure: attention latency overhead ------------------
+    # With speculation a layer's attention costs the approximation where it
+    # commits and exact attention where it discards; without, always exact
+    # attention.  Per-layer device times of back-to-back layers captured as
+    # HIP graphs: exact attention alone (the exact-only baseline) and the
+    # approximation alone (the static-sink baseline).
+    if "exact_only_baseline" in res and "static_sink_baseline" in res:
+        t_e = res["exact_only_baseline"]["ms_per_step"] * 1e3 / nl
+        t_a = res["static_sink_baseline"]["ms_per_step"] * 1e3 / nl
+        out["attention_overhead_reduction"] = {
+            "value": overhead_reduction(t_e, t_a, hit_rate),
+            "by_needles": {n_: overhead_reduction(t_e, t_a, h_)
+                           for n_, h_ in hits.items()},
+            "t_exact_us": t_e, "t_approx_us": t_a, "hit_rate": hit_rate,
+            "approx_over_exact": t_a / t_e,
+            "formula": "t_exact / (hit_rate * t_approx + (1 - hit_rate) "
+                       "* t_exact)",
+            "inputs": "per-layer device time of back-to-back layers "
+                      "captured as HIP graphs: exact attention alone "
+                      "(exact_only_baseline) and the approximation alone "
+                      "(static_sink_baseline); hit rate of this run"}
+    for key in ("pipelined", "sequential"):
+        r_ = res.get(key, {})
+        if "approx_latency_us_mean" in r_:
+            r_["attention_overhead_reduction"] = overhead_reduction(
+                r_["exact_latency_us_mean"], r_["approx_latency_us_mean"],
+                hit_rate)
     if "exact_only_baseline" in res:
         # time a speculative step costs over exact attention alone
         out["speculation_cost_frac"] = (
@@ -585,13 +617,20 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, works, dens, outs, nl, Qs,
                                            Ks, Vs)
 
+    # ---- the other configurations (headline inputs freed first) ---------
+    del graphs
+    Ks.clear()
+    Vs.clear()
+    A.clear()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    which = [c for c in args.configs.split(",") if c and c != "none"]
+    if which:
+        out["configs"] = config_records(args, al, B_, h, dev, which)
+        log("configurations done")
+
     # ---- HBM probe ------------------------------------------------------
     if not args.no_probe:
-        del graphs
-        Ks.clear()
-        Vs.clear()
-        A.clear()
-        torch.cuda.synchronize()
         torch.cuda.empty_cache()
         pr = sdev.probe_bandwidth()
         out["probe"] = {k: round(v["GBps"], 1) for k, v in pr.items()}
@@ -604,55 +643,147 @@ def main():
     h.close()
 
 
-# Assumed xGMI figures for the projection (no second GPU here): latency of
-# a small point-to-point transfer (a commit flag or an 8-16 KiB output) and
-# of a small all-reduce across the GPUs of a tensor-parallel group.
-XGMI_P2P_US = 5.0
-XGMI_ALLREDUCE_US = 10.0
+def overhead_reduction(t_exact, t_approx, hit):
+    """The pages' attention latency overhead reduction ("Attention-Level
+    Speculation", atlas.scime.ai summary, Key results): attention costs
+    t_exact per layer without speculation; with it, t_approx where the
+    speculation commits (a fraction `hit` of the layers) and t_exact where
+    it discards."""
+    return t_exact / (hit * t_approx + (1.0 - hit) * t_exact)
+
+
+# Link latencies swept by the projection (no second GPU here): a small
+# point-to-point transfer (a commit flag or an 8-16 KiB output) and a small
+# all-reduce of a tensor-parallel pair, both taken as one latency L.
+LINK_US = (2.0, 5.0, 10.0, 20.0)
+
+
+def project_layer(t_approx, t_exact, exact_only, post, hit, p2p, allreduce):
+    """Per-layer latency of one decode token on two GPUs, projected from
+    one GPU's measured durations, as the pages projected H100 ([A] Key
+    results, Limitations: device durations, host and dispatch latency
+    excluded):
+      one_gpu  exact attention, then post-attention, in turn;
+      alspec   the pages' placement ([A] Approach): GPU A runs exact
+               attention and the verify, GPU B the approximation and the
+               post-attention work on it.  A commit costs max(approx + post,
+               exact to verified output + p2p); a discard costs exact + p2p
+               + the replayed post-attention work; weighted by the hit rate;
+      tp2      tensor parallel over two GPUs, no speculation: attention and
+               post-attention each halved, plus two all-reduces (after the
+               output projection and after the MLP)."""
+    one = exact_only + post
+    commit = max(t_approx + post, t_exact + p2p)
+    discard = t_exact + p2p + post
+    alspec = hit * commit + (1.0 - hit) * discard
+    tp2 = (exact_only + post) / 2.0 + 2.0 * allreduce
+    return {"one_gpu": one, "alspec_2gpu_commit": commit,
+            "alspec_2gpu_discard": discard, "alspec_2gpu": alspec,
+            "tp_2gpu": tp2}
 
 
 def projection(seq, exact_only_us, post_us, hit):
-    """Per-layer latency of one decode token projected from this run's
-    MI355X kernel durations to placements on two GPUs, as the pages
-    projected H100 from measured durations ([A] Key results, Limitations):
-    host and dispatch latency excluded, link figures assumed.
-      one_gpu          exact attention, then post-attention, in turn
-      alspec_2gpu      the pages' placement: GPU A runs exact attention and
-                       the verify; GPU B runs the approximation and the
-                       post-attention work on it and goes on to the next
-                       layer.  Commit: the two run side by side, so a layer
-                       costs max(approx + post, exact to verified output +
-                       link).  Discard: B waits for the exact output, then
-                       replays the post-attention work.
-      tp_2gpu          tensor parallel over two GPUs, no speculation:
-                       attention and post-attention each halved, plus the
-                       two all-reduces of a decoder layer (after the output
-                       projection and after the MLP)."""
+    """project_layer over the swept link latencies, from this run's
+    sequential-schedule latencies, exact-only attention and post-attention
+    duration (MI355X, one GPU)."""
     t_a = seq["approx_latency_us_mean"]
     t_e = seq["exact_latency_us_mean"]
-    one = exact_only_us + post_us
-    commit = max(t_a + post_us, t_e + XGMI_P2P_US)
-    discard = t_e + XGMI_P2P_US + post_us
-    alspec = hit * commit + (1.0 - hit) * discard
-    tp2 = (exact_only_us + post_us) / 2.0 + 2 * XGMI_ALLREDUCE_US
+    sweep = []
+    for L in LINK_US:
+        u = project_layer(t_a, t_e, exact_only_us, post_us, hit, L, L)
+        sweep.append({"link_us": L, "us_per_layer": u,
+                      "speedup_vs_one_gpu": {
+                          "alspec_2gpu": u["one_gpu"] / u["alspec_2gpu"],
+                          "tp_2gpu": u["one_gpu"] / u["tp_2gpu"]}})
     return {
         "inputs_us": {"approximation": t_a,
                       "exact_to_verified_output": t_e,
                       "exact_only_attention": exact_only_us,
-                      "post_attention": post_us,
-                      "assumed_xgmi_p2p": XGMI_P2P_US,
-                      "assumed_xgmi_allreduce": XGMI_ALLREDUCE_US},
+                      "post_attention": post_us},
         "hit_rate": hit,
-        "us_per_layer": {"one_gpu": one, "alspec_2gpu_commit": commit,
-                         "alspec_2gpu_discard": discard,
-                         "alspec_2gpu": alspec, "tp_2gpu": tp2},
-        "speedup_vs_one_gpu": {"alspec_2gpu": one / alspec,
-                               "tp_2gpu": one / tp2},
+        "link_sweep": sweep,
         "note": "a model, not a measurement: durations measured on one "
-                "MI355X, the link figures assumed; the post-attention "
-                "weights are random, the hit rate is this run's attention "
-                "hit rate on the synthetic inputs",
+                "MI355X, the link latency swept (point-to-point and "
+                "all-reduce both taken as it); the post-attention weights "
+                "are random, the hit rate is this run's attention hit rate "
+                "on the synthetic inputs",
     }
+
+
+def config_records(args, al, B_, h, dev, which):
+    """The other configurations as layer-pipelined chains
+    (alspec_spec_decode_layers), one at a time, each drawn on the device and
+    freed after: the chain's wall time per decode token (HIP events around
+    back-to-back chains of all layers), its steady launch against the HBM
+    roofline (as for the headline), and the hit rate."""
+    import torch
+
+    from synth import device as sdev
+    from synth import gen
+    recs = {}
+    for name in which:
+        w = {"c2": gen.llama8b_32k, "c4": gen.multiuser_8b,
+             "c5": gen.llama70b_128k}[name]()
+        nl = w.n_layers
+        t0 = time.time()
+        K = torch.empty((nl, w.B, w.Hkv, w.L_cap, w.D), dtype=torch.bfloat16,
+                        device=dev)
+        V = torch.empty_like(K)
+        Q = torch.empty((nl, w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+        for layer in range(nl):
+            sdev.fill_kv(w, layer, K[layer], V[layer])
+            Q[layer].copy_(torch.from_numpy(gen.q_all(w, layer)))
+        torch.cuda.synchronize()
+        log(f"{name}: drew {nl} layers ({2 * K.numel() * 2 / 2**30:.1f} GiB) "
+            f"t={time.time() - t0:.1f}s")
+        p = al.params_for(w)
+        wss = [al.alloc_workspace(p, dev) for _ in range(3)]
+        outs = [al.alloc_outputs(p, dev) for _ in range(nl)]
+        arr = B_.layers_struct(p, [(Q[l], K[l], V[l], outs[l], wss[l % 3])
+                                   for l in range(nl)])
+        s = torch.cuda.Stream(device=dev)
+        steady, reps = chain_timing(args, B_, h, p, [arr], s, nl)
+        # whole chains, back to back
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            st = B_._spec_decode_layers(h.ptr, ctypes.byref(p), nl, arr,
+                                        s.cuda_stream)
+            if st != 0:
+                raise al.AlspecError(st, "alspec_spec_decode_layers")
+        e1.record(s)
+        torch.cuda.synchronize()
+        chain_us = e0.elapsed_time(e1) * 1e3 / reps
+        layer_bytes = sum(w.seq_lens) * w.Hkv * w.D * 2 * 2
+        ratio = torch.stack([o["ratio"] for o in outs]).cpu().numpy()
+        achieved = layer_bytes / (steady * 1e-6) / 1e9
+        lams = (0.05, 0.10, 0.20) if name == "c4" else (w.lam,)
+        recs[name] = {
+            "workload": f"{w.name}: batch {w.B}, {w.Hq} q / {w.Hkv} kv heads, "
+                        f"head dim {w.D}, bf16 KV, context "
+                        f"{min(w.seq_lens)}-{max(w.seq_lens)}, sink {w.S}, "
+                        f"window {w.W}, {nl} layers",
+            "schedule": "layer_pipelined (alspec_spec_decode_layers, "
+                        "eager, one call per decode token)",
+            "tokens_layers_per_s": w.B * nl / (chain_us * 1e-6),
+            "us_per_layer": chain_us / nl,
+            "chains_timed": reps,
+            "roofline": {"bound": "hbm", "achieved": achieved,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "chain_kernel (steady state)",
+                         "algorithmic_bytes_per_launch": layer_bytes,
+                         "launch_us_mean": steady},
+            "hit_rate": {str(lam): float((ratio <= lam).mean())
+                         for lam in lams},
+        }
+        log(f"{name}: {recs[name]['us_per_layer']:.1f} us per layer, steady "
+            f"launch {steady:.1f} us ({achieved / HBM_PEAK_GBPS:.3f} of peak)")
+        del K, V, Q, outs, wss, arr
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return recs
 
 
 def model_timing(args, al, h, w, Q, K, V, nl, dev):
