@@ -6,7 +6,8 @@ include/alspec.h (libalspec.so, built in-tree); this package is the thin
 Python binding over it.  Importing fails if the library is not built.
 """
 from ._binding import (AlspecError, Events, Handle, KV_BF16, KV_F32,
-                       LIB_PATH, NOALLOC_SCRATCH_BYTES, POST_MAX_BATCH,
+                       LAYERS_WS_RING, LIB_PATH, NOALLOC_SCRATCH_BYTES,
+                       POST_MAX_BATCH,
                        Params, PostParams, PostWeights, alloc_outputs, alloc_post_workspace,
                        alloc_workspace, make_post_params, post_attention,
                        post_weights_struct, post_workspace_size,
@@ -18,7 +19,8 @@ from ._binding import (AlspecError, Events, Handle, KV_BF16, KV_F32,
                        status_string, verify, version, workspace_size)
 
 __all__ = ["AlspecError", "Events", "Handle", "KV_BF16", "KV_F32",
-           "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "POST_MAX_BATCH", "Params",
+           "LAYERS_WS_RING", "LIB_PATH", "NOALLOC_SCRATCH_BYTES",
+           "POST_MAX_BATCH", "Params",
            "PostParams",
            "PostWeights", "alloc_outputs", "alloc_post_workspace",
            "alloc_workspace", "make_post_params", "post_attention",

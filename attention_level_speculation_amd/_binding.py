@@ -28,6 +28,9 @@ STATUS = {0: "ALSPEC_OK", 1: "ALSPEC_ERR_INVALID_ARG",
           2: "ALSPEC_ERR_UNSUPPORTED", 3: "ALSPEC_ERR_WORKSPACE",
           4: "ALSPEC_ERR_HIP"}
 MAX_BATCH = 64
+# ALSPEC_LAYERS_WS_RING: layers fewer than this apart in one
+# spec_decode_layers call must not share a workspace
+LAYERS_WS_RING = 3
 
 # One HIP runtime per process: torch ships its own libamdhip64 (same SONAME
 # as the system one).  Loading torch first makes this library bind to the

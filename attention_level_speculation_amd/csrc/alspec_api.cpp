@@ -546,13 +546,56 @@ alspec_status alspec_spec_decode_layers(alspec_handle *h,
         ALSPEC_OK)
       return st;
     if ((st = check_ws(L.ws, L.ws_bytes, wl)) != ALSPEC_OK) return st;
-    // a workspace is in use from the launch before its layer's to the one
-    // after it
+    // A workspace is in use from the launch before its layer's to the one
+    // after it.  In the one-launch form a layer's splits wait for the verify
+    // of the layer before on the same workspace, which the queue places
+    // ahead of them only if that layer is at least three back.
     for (int d = 1; d <= 2 && j + d < n_layers; ++d)
       if (layers[j + d].ws == L.ws) return ALSPEC_ERR_WORKSPACE;
   }
   const float sm_log2 = p->sm_scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
+  if (p->overlap != 1) {
+    // One launch per kChainMaxLayers layers, each self-contained, after the
+    // table of its layers has been written into its first layer's
+    // workspace by a small kernel on the same stream.
+    for (int a = 0; a < n_layers; a += alspec::kChainMaxLayers) {
+      const int n = n_layers - a < alspec::kChainMaxLayers
+                        ? n_layers - a
+                        : alspec::kChainMaxLayers;
+      alspec::ChainEntry tab[alspec::kChainMaxLayers];
+      for (int j = 0; j < n; ++j) {
+        const alspec_layer &L = layers[a + j];
+        int prev = -1;
+        for (int i = j - 1; i >= 0 && prev < 0; --i)
+          if (layers[a + i].ws == L.ws) prev = i;
+        tab[j] = alspec::ChainEntry{L.q,          L.k,       L.v,
+                                    (char *)L.ws, L.o_approx, L.lse_approx,
+                                    L.o_exact,    L.lse_exact, L.ratio,
+                                    L.commit,     L.o_committed, prev, 0};
+      }
+      char *ws0 = (char *)layers[a].ws;
+      alspec::OneChainArgs ca;
+      ca.n = n;
+      ca.lambda = p->lambda;
+      ca.ctl = ws0 + wl.off_chain_ctl;
+      ca.table = (const alspec::ChainEntry *)(ws0 + wl.off_chain_table);
+      ca.off_counters = (unsigned)wl.off_counters;
+      ca.off_part_ml = (unsigned)wl.off_part_ml;
+      ca.off_part_acc = (unsigned)wl.off_part_acc;
+      ca.off_stA_ml = (unsigned)wl.off_stA_ml;
+      ca.off_stA_acc = (unsigned)wl.off_stA_acc;
+      ca.off_headnd = (unsigned)wl.off_headnd;
+      if (failed(alspec::launch_chain_table(
+                     tab, n, (alspec::ChainEntry *)(ws0 + wl.off_chain_table),
+                     s),
+                 "launch_chain_table") ||
+          failed(alspec::launch_one_chain(pa, p->kv_dtype, ca, sm_log2, s),
+                 "launch_one_chain"))
+        return ALSPEC_ERR_HIP;
+    }
+    return ALSPEC_OK;
+  }
   auto chain_layer = [&](int j) {
     const alspec_layer &L = layers[j];
     alspec::ChainLayer c;

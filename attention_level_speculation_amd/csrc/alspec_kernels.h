@@ -79,6 +79,55 @@ hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
                         const ChainLayer *ver, bool merge_mid, float sm_log2,
                         hipStream_t s);
 
+// One layer of the one-launch chain, as its entry in the layer table: its
+// inputs, the base of its workspace (the layout is the plan's), its
+// outputs, and the latest earlier layer of the chain on the same workspace
+// (-1 if none).
+struct ChainEntry {
+  const float *q;
+  const void *k, *v;
+  char *ws;
+  float *o_approx, *lse_approx, *o_exact, *lse_exact, *ratio;
+  uint8_t *commit;
+  float *o_committed;
+  int prev;
+  int unused;
+};
+static_assert(sizeof(ChainEntry) == kChainEntryBytes, "table entry");
+
+// The one-launch chain over the n layers of `table` (device), with its
+// control block at `ctl` (device, zero when the launch starts; zero again
+// when it ends).
+struct OneChainArgs {
+  int n;
+  float lambda;
+  char *ctl;
+  const ChainEntry *table;
+  unsigned off_counters, off_part_ml, off_part_acc, off_stA_ml, off_stA_acc,
+      off_headnd;
+};
+
+// Copies n host-side entries into the device table at dst (kernel
+// arguments, so no host memory needs to stay valid after the call).
+hipError_t launch_chain_table(const ChainEntry *src, int n, ChainEntry *dst,
+                              hipStream_t s);
+
+// The launch itself: one block per queue item.
+hipError_t launch_one_chain(const PlanArgs &pa, int kv_dtype,
+                            const OneChainArgs &ca, float sm_log2,
+                            hipStream_t s);
+
+// Length of the one-launch chain's queue (host): the first layer's sink and
+// window splits, then per layer s of n: its merge of sink and window
+// states, the next layer's sink and window splits (but after the last
+// layer), its middle splits and the verify of the layer before (but for
+// the first layer); then the last layer's verify.
+inline int one_chain_items(const PlanArgs &pa, int n) {
+  const int nG = pa.B * pa.Hkv, nA = pa.itemA_pre[pa.B];
+  const int nM = pa.itemM_pre[pa.B], nV = pa.B * pa.Hq / pa.NHv;
+  return nA + n * (nG + nM) + (n - 1) * (nA + nV) + nV;
+}
+
 // Standalone verify of two output buffers.
 hipError_t launch_verify(const PlanArgs &pa, const float *o_approx,
                          const float *o_exact, float *ratio, uint8_t *commit,

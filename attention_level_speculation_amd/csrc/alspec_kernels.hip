@@ -73,6 +73,38 @@ __device__ __forceinline__ void put_f2(float2 *p, float2 v) {
     *p = v;
 }
 
+// Loads of values another block of the same launch stored with put_f /
+// put_f2 (CO): agent-scope relaxed atomic loads, which read the coherent
+// copy, so the reader needs no acquire fence (an invalidation of its whole
+// L2, which disturbs every block streaming through it).
+template <bool CO>
+__device__ __forceinline__ float get_f(const float *p) {
+  if constexpr (CO)
+    return __uint_as_float(__hip_atomic_load(
+        (const unsigned *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  else
+    return *p;
+}
+template <bool CO>
+__device__ __forceinline__ float2 get_f2(const float2 *p) {
+  if constexpr (CO)
+    return __builtin_bit_cast(
+        float2, __hip_atomic_load((const unsigned long long *)p,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  else
+    return *p;
+}
+template <bool CO>
+__device__ __forceinline__ float4 get_f4(const float4 *p) {
+  if constexpr (CO) {
+    const float2 a = get_f2<true>((const float2 *)p);
+    const float2 b = get_f2<true>((const float2 *)p + 1);
+    return make_float4(a.x, a.y, b.x, b.y);
+  } else {
+    return *p;
+  }
+}
+
 // ---------------------------------------------------------------- types ---
 
 struct KvF32 {
@@ -184,7 +216,7 @@ __device__ __forceinline__ float wave_max(float x) { return group_max<64>(x); }
 // independent online softmax; the groups and waves are merged at the end.
 // Writes (m, l) to out_ml[h * ml_stride] and acc to out_acc[h * D + d].
 template <class KV, int D, int G, bool CO = false>
-__device__ void split_state(const float *__restrict__ qg,
+__device__ __forceinline__ void split_state(const float *__restrict__ qg,
                             const typename KV::elem *__restrict__ kb,
                             const typename KV::elem *__restrict__ vb, int t0,
                             int t1, float sm_log2, float2 *__restrict__ out_ml,
@@ -661,7 +693,7 @@ struct MfmaWave {
 // another, so a wait covers only the loads of the tile about to be used.
 // Each wave keeps its own online softmax; the waves are merged at the end.
 template <int G, int NS, bool CO = false>
-__device__ void split_state_mfma(const float *__restrict__ qg,
+__device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
                                  const uint16_t *__restrict__ kb,
                                  const uint16_t *__restrict__ vb, int t0,
                                  int t1, float sm_log2,
@@ -727,7 +759,7 @@ __device__ void split_state_mfma(const float *__restrict__ qg,
 // tiles, arithmetic and order as split_state_mfma, so the same bits.  The
 // range must be nonempty (every split of the plan is).
 template <int G, int NT, bool CO>
-__device__ void split_state_mfma_short(const float *__restrict__ qg,
+__device__ __forceinline__ void split_state_mfma_short(const float *__restrict__ qg,
                                        const uint16_t *__restrict__ kb,
                                        const uint16_t *__restrict__ vb,
                                        int t0, int t1, float sm_log2,
@@ -767,7 +799,7 @@ __device__ void split_state_mfma_short(const float *__restrict__ qg,
 // its loads (which also cover every slot's max) before using any.  Larger
 // n takes a max pass and then rounds of NSG * R slots.  On return
 // res_acc[NH][D], res_m[NH], res_l[NH] (shared) hold the merged states.
-template <int D, int NH, int R>
+template <int D, int NH, int R, bool CO = false>
 __device__ void merge_heads(const float2 *__restrict__ ml,
                             const float *__restrict__ acc, int slot0, int n,
                             int Hq, int h0, bool has_prior,
@@ -794,8 +826,8 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
   // read whether or not it is used, so no load sits behind a branch.
   float2 mv[R];
   float4 av[R];
-  const float2 pml_raw = prior_ml[has_prior ? hh : 0];
-  const float pacc_raw = prior_acc[has_prior && t < NH * D ? t : 0];
+  const float2 pml_raw = get_f2<CO>(&prior_ml[has_prior ? hh : 0]);
+  const float pacc_raw = get_f<CO>(&prior_acc[has_prior && t < NH * D ? t : 0]);
   const float2 pml = has_prior ? pml_raw : make_float2(neg_inf(), 0.f);
   const float pacc = has_prior ? pacc_raw : 0.f;
   float mx = pml.x;
@@ -804,15 +836,15 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
     for (int k = 0; k < R; ++k) {
       const int i = min(sg + k * NSG, n - 1);
       const size_t sl = (size_t)(slot0 + i) * Hq + h;
-      mv[k] = ml[sl];
-      av[k] = ((const float4 *)(acc + sl * D))[c];
+      mv[k] = get_f2<CO>(&ml[sl]);
+      av[k] = get_f4<CO>((const float4 *)(acc + sl * D) + c);
     }
 #pragma unroll
     for (int k = 0; k < R; ++k)
       if (sg + k * NSG < n) mx = fmaxf(mx, mv[k].x);
   } else if (!one_round) {
     for (int i = u; i < n; i += TPH)
-      mx = fmaxf(mx, ml[(size_t)(slot0 + i) * Hq + h].x);
+      mx = fmaxf(mx, get_f2<CO>(&ml[(size_t)(slot0 + i) * Hq + h]).x);
   }
   mx = group_max<(TPH < 64 ? TPH : 64)>(mx);
   if (TPH >= 64) {
@@ -835,8 +867,8 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
         const int i = base + k * NSG;
         if (i < n) {
           const size_t sl = (size_t)(slot0 + i) * Hq + h;
-          mv[k] = ml[sl];
-          av[k] = ((const float4 *)(acc + sl * D))[c];
+          mv[k] = get_f2<CO>(&ml[sl]);
+          av[k] = get_f4<CO>((const float4 *)(acc + sl * D) + c);
         }
       }
     }
@@ -863,8 +895,8 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
     for (int w = 1; w < WPH; ++w) Mh = fmaxf(Mh, s_mx[h2][w]);
     float tot = 0.f;
     if (has_prior) {
-      const float pa = (idx == t) ? pacc : prior_acc[idx];
-      tot = pa * fast_exp2(prior_ml[h2].x - exp_ref(Mh));
+      const float pa = (idx == t) ? pacc : get_f<CO>(&prior_acc[idx]);
+      tot = pa * fast_exp2(get_f2<CO>(&prior_ml[h2]).x - exp_ref(Mh));
     }
 #pragma unroll
     for (int g = 0; g < NSG; ++g) tot += ((const float *)&s_pacc[h2][g][0])[d];
@@ -874,8 +906,11 @@ __device__ void merge_heads(const float2 *__restrict__ ml,
     float Mh = s_mx[t][0];
 #pragma unroll
     for (int w = 1; w < WPH; ++w) Mh = fmaxf(Mh, s_mx[t][w]);
-    float tl = has_prior ? prior_ml[t].y * fast_exp2(prior_ml[t].x - exp_ref(Mh))
-                         : 0.f;
+    float tl = 0.f;
+    if (has_prior) {
+      const float2 pm = get_f2<CO>(&prior_ml[t]);
+      tl = pm.y * fast_exp2(pm.x - exp_ref(Mh));
+    }
 #pragma unroll
     for (int g = 0; g < NSG; ++g) tl += s_pl[t][g];
     res_l[t] = tl;
@@ -955,6 +990,7 @@ __device__ bool arrive_last(unsigned *cnt, unsigned total) {
 // thread 0 takes the device-scope acquire (invalidating stale copies this
 // CU and its L2 may hold) before the barrier that lets the block read the
 // states with ordinary loads.
+template <bool ACQ = true>
 __device__ bool arrive_last_coherent(unsigned *cnt, unsigned total) {
   __shared__ int s_last;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -966,7 +1002,7 @@ __device__ bool arrive_last_coherent(unsigned *cnt, unsigned total) {
     const int last = (old == total - 1) ? 1 : 0;
     if (last) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     s_last = last;
   }
@@ -1050,7 +1086,7 @@ __device__ __forceinline__ void split_any(const float *qg,
 // Per-head sums of the relative L2 test over a block's G x D outputs, kept
 // in fixed order: each wave sums one head's slice of a pass, then the
 // waves of a head are added in order.
-template <int D, int G>
+template <int D, int G, bool CO = false>
 __device__ void group_num_den(const float *e, const float *a, float *num,
                               float *den) {
   constexpr int WPH = D / 64;          // waves per head in one pass
@@ -1063,7 +1099,7 @@ __device__ void group_num_den(const float *e, const float *a, float *num,
     const int idx = p * kThreads + threadIdx.x;
     float n = 0.f, d2 = 0.f;
     if (idx < G * D) {
-      const float diff = a[idx] - e[idx];
+      const float diff = get_f<CO>(&a[idx]) - e[idx];
       n = diff * diff;
       d2 = e[idx] * e[idx];
     }
@@ -1094,7 +1130,7 @@ __device__ void group_num_den(const float *e, const float *a, float *num,
 // sink+window state merged with the middle slots, normalised into o_exact
 // (and lse_exact); each head's (num, den) of the verify goes to the
 // workspace.
-template <int D, int NH, bool VERIFY = true>
+template <int D, int NH, bool VERIFY = true, bool CO = false>
 __device__ void exact_heads(const PlanArgs &pa, const WsPtrs &w, int b,
                             int h0, const float *__restrict__ o_approx,
                             float *__restrict__ o_exact,
@@ -1105,30 +1141,31 @@ __device__ void exact_heads(const PlanArgs &pa, const WsPtrs &w, int b,
   const int Hq = pa.Hq;
   const size_t bh0 = (size_t)b * Hq + h0;
   const int nA = pa.nsink[b] + pa.nwin[b];
-  merge_heads<D, NH, kMergeRoundM>(w.part_ml, w.part_acc,
-                                   pa.slot_base[b] + nA, pa.nmid[b], Hq, h0,
-                                   true, w.stA_ml + bh0, w.stA_acc + bh0 * D,
-                                   r_acc, r_m, r_l);
+  merge_heads<D, NH, kMergeRoundM, CO>(w.part_ml, w.part_acc,
+                                       pa.slot_base[b] + nA, pa.nmid[b], Hq,
+                                       h0, true, w.stA_ml + bh0,
+                                       w.stA_acc + bh0 * D, r_acc, r_m, r_l);
   for (int idx = threadIdx.x; idx < NH * D; idx += kThreads) {
     const float e = normalise(r_acc[idx], r_l[idx / D]);
     r_acc[idx] = e;
-    o_exact[bh0 * D + idx] = e;
+    put_f<CO>(&o_exact[bh0 * D + idx], e);
   }
   __syncthreads();
   if constexpr (VERIFY) {
-    group_num_den<D, NH>(r_acc, o_approx + bh0 * D, s_num, s_den);
+    group_num_den<D, NH, CO>(r_acc, o_approx + bh0 * D, s_num, s_den);
     __syncthreads();
   }
   if (threadIdx.x < NH) {
     const int hh = threadIdx.x;
-    if constexpr (VERIFY) w.headnd[bh0 + hh] = make_float2(s_num[hh], s_den[hh]);
+    if constexpr (VERIFY)
+      put_f2<CO>(&w.headnd[bh0 + hh], make_float2(s_num[hh], s_den[hh]));
     if (lse_exact) lse_exact[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
   }
 }
 
 // Per-entry verdict once every head of entry b has stored its (num, den): ratio over all heads (summed in head order), commit flag,
 // committed output.
-template <int D>
+template <int D, bool CO = false>
 __device__ void finalize_entry(const PlanArgs &pa, const WsPtrs &w, int b,
                                const float *__restrict__ o_approx,
                                const float *__restrict__ o_exact,
@@ -1140,7 +1177,7 @@ __device__ void finalize_entry(const PlanArgs &pa, const WsPtrs &w, int b,
   const int Hq = pa.Hq;
   float n = 0.f, d2 = 0.f;
   for (int h = threadIdx.x; h < Hq; h += kThreads) {
-    const float2 nd = w.headnd[(size_t)b * Hq + h];
+    const float2 nd = get_f2<CO>(&w.headnd[(size_t)b * Hq + h]);
     n += nd.x;
     d2 += nd.y;
   }
@@ -1164,7 +1201,7 @@ __device__ void finalize_entry(const PlanArgs &pa, const WsPtrs &w, int b,
       float4 v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        v[k] = src[min(base + k * kThreads, n4 - 1)];
+        v[k] = get_f4<CO>(&src[min(base + k * kThreads, n4 - 1)]);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (base + k * kThreads < n4) dst[base + k * kThreads] = v[k];
@@ -1218,7 +1255,7 @@ __global__ __launch_bounds__(kThreads) void partials_all_kernel(
 // reusable merged state and (each if non-null) o_approx / lse_approx.  The
 // exact combines start from that state, so with an empty middle they give
 // the approximation's bits.
-template <int D, int G>
+template <int D, int G, bool CO = false>
 __device__ void approx_merge(const PlanArgs &pa, const WsPtrs &w,
                              const Outs &o, int b, int g) {
   __shared__ float r_acc[G * D];
@@ -1228,19 +1265,20 @@ __device__ void approx_merge(const PlanArgs &pa, const WsPtrs &w,
   const int nA = pa.nsink[b] + pa.nwin[b];
   const size_t bh0 = (size_t)b * Hq + h0;
   // no prior state; the stored-state slots only serve as valid addresses
-  merge_heads<D, G, kMergeRoundA>(w.part_ml, w.part_acc,
+  merge_heads<D, G, kMergeRoundA, CO>(w.part_ml, w.part_acc,
                                       pa.slot_base[b], nA, Hq, h0, false,
                                       w.stA_ml + bh0, w.stA_acc + bh0 * D,
                                       r_acc, r_m, r_l);
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D;
-    w.stA_acc[bh0 * D + idx] = r_acc[idx];
-    if (o.o_approx) o.o_approx[bh0 * D + idx] = normalise(r_acc[idx], r_l[hh]);
+    put_f<CO>(&w.stA_acc[bh0 * D + idx], r_acc[idx]);
+    if (o.o_approx)
+      put_f<CO>(&o.o_approx[bh0 * D + idx], normalise(r_acc[idx], r_l[hh]));
   }
   if (threadIdx.x < G) {
     const int hh = threadIdx.x;
-    w.stA_ml[bh0 + hh] = make_float2(r_m[hh], r_l[hh]);
-    if (o.lse_approx) o.lse_approx[bh0 + hh] = lse_nat(r_m[hh], r_l[hh]);
+    put_f2<CO>(&w.stA_ml[bh0 + hh], make_float2(r_m[hh], r_l[hh]));
+    if (o.lse_approx) put_f<CO>(&o.lse_approx[bh0 + hh], lse_nat(r_m[hh], r_l[hh]));
   }
 }
 
@@ -1390,6 +1428,232 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(
                             it.t0, it.t1, sm_log2,
                             L.w.part_ml + (size_t)it.slot * Hq + h0,
                             L.w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+}
+
+// --------------------------------------------------- one-launch chain ---
+
+// Waits of one block for another's items poll at most this often, about
+// 1.7 us apart (about a second in all); a wait that runs out counts itself
+// in the launch's error counter and goes on, so no wave ever waits without
+// end.  The waits last tens of microseconds; polling less often keeps the
+// waiting blocks' loads of one counter line off the memory system that the
+// streaming blocks use.
+constexpr unsigned kChainSpinLimit = 1u << 19;
+
+// Thread 0 waits until *cnt reaches target; the barrier then lets the block
+// read what the counted items stored, with agent-scope loads (no acquire
+// fence: its L2 invalidation would disturb the blocks streaming beside).
+__device__ void chain_wait(unsigned *cnt, unsigned target, unsigned *err) {
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           target) {
+      __builtin_amdgcn_s_sleep(64);
+      if (++spins > kChainSpinLimit) {
+        __hip_atomic_fetch_add(err, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Counts one finished item whose results the block stored with agent-scope
+// atomic stores: every thread waits for its stores' completion, then
+// thread 0 adds one.
+__device__ void chain_signal(unsigned *cnt) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// verify_block for a launch whose other blocks run the same layer's items:
+// the exact outputs and per-head sums go out as agent-scope atomic stores
+// and the entry's last block takes them over without a cache write-back.
+template <int D, int NH>
+__device__ void verify_block_co(const PlanArgs &pa, const WsPtrs &w,
+                                const Outs &o, int idx) {
+  const int per = pa.Hq / NH;
+  const int b = idx / per, h0 = (idx % per) * NH;
+  exact_heads<D, NH, true, true>(pa, w, b, h0, o.o_approx, o.o_exact,
+                                 o.lse_exact);
+  if (!arrive_last_coherent<false>(user_counter(w, b), (unsigned)per))
+    return;
+  finalize_entry<D, true>(pa, w, b, o.o_approx, o.o_exact, o.ratio, o.commit,
+                          o.o_committed, o.lambda);
+}
+
+__device__ __forceinline__ WsPtrs chain_ws(const OneChainArgs &ca,
+                                           char *base) {
+  WsPtrs w;
+  w.counters = (unsigned *)(base + ca.off_counters);
+  w.part_ml = (float2 *)(base + ca.off_part_ml);
+  w.part_acc = (float *)(base + ca.off_part_acc);
+  w.stA_ml = (float2 *)(base + ca.off_stA_ml);
+  w.stA_acc = (float *)(base + ca.off_stA_acc);
+  w.headnd = (float2 *)(base + ca.off_headnd);
+  return w;
+}
+
+// Control block: queue (line 0), finished blocks (line 1), errors (line 2),
+// then per layer j one line with its finished sink/window splits, middle
+// splits, merges and verifies.
+__device__ __forceinline__ unsigned *chain_line(const OneChainArgs &ca,
+                                                int line) {
+  return (unsigned *)ca.ctl + line * kCounterStride;
+}
+enum ChainCount { kCntA = 0, kCntM = 8, kCntG = 16, kCntV = 24 };
+__device__ __forceinline__ unsigned *chain_count(const OneChainArgs &ca,
+                                                 int layer, ChainCount c) {
+  return chain_line(ca, 3 + layer) + c;
+}
+
+// A chain of independent layers in one launch, one block per item of the
+// queue (one_chain_items):
+//   the sink and window splits of layer 0, then for each layer s:
+//     the merge of layer s's sink and window states   (waits: its splits)
+//     the sink and window splits of layer s+1          (waits: see below)
+//     the middle splits of layer s                     (waits: see below)
+//     the exact merge, verify and commit of layer s-1  (waits: its middle
+//                                                       splits and merge)
+//   then the verify of the last layer.
+// A block takes the next item with one atomic add when it starts, not the
+// item of its index, so the XCDs whose blocks stream faster take more of
+// the items, and no layer's slowest blocks hold up the next layer's middle
+// splits: the launch ends once, after the last layer.  (The hardware deals
+// block indices to the XCDs in turn, so items fixed by index would keep
+// each XCD's share fixed.)  A layer's splits first wait until the latest
+// earlier layer on the same workspace has finished its verify.  Every wait
+// is for items earlier in the queue, so for blocks already running, and is
+// bounded.  Every item runs the same code as in the per-layer launches, so
+// the bits are the same.  The last block to finish resets the control
+// block (but the error count, kept for inspection).
+template <class KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void one_chain_kernel(PlanArgs pa,
+                                                             OneChainArgs ca,
+                                                             float sm_log2) {
+  using E = typename KV::elem;
+  __shared__ int s_item;
+  unsigned *err = chain_line(ca, 2);
+  const int nG = pa.B * pa.Hkv;
+  const int nA = pa.itemA_pre[pa.B];
+  const int nM = pa.itemM_pre[pa.B];
+  const int nV = pa.B * pa.Hq / pa.NHv;
+  const int n = ca.n;
+  const int Hq = pa.Hq;
+  if (threadIdx.x == 0)
+    s_item = (int)__hip_atomic_fetch_add(chain_line(ca, 0), 1u,
+                                         __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // the item is the same for the whole block: keep it (and every index and
+  // branch derived from it) scalar
+  int k = __builtin_amdgcn_readfirstlane(s_item);
+  // kind: 0 merge, 1 sink/window split, 2 middle split, 3 verify; layer
+  int kind, layer;
+  if (k < nA) {
+    kind = 1;
+    layer = 0;
+  } else {
+    k -= nA;
+    int s = 0;
+    kind = 3;
+    layer = n - 1;  // past every segment: the last layer's verify
+    for (; s < n; ++s) {
+      const int a = s + 1 < n ? nA : 0;
+      const int v = s > 0 ? nV : 0;
+      if (k < nG) {
+        kind = 0;
+        layer = s;
+        break;
+      }
+      k -= nG;
+      if (k < a) {
+        kind = 1;
+        layer = s + 1;
+        break;
+      }
+      k -= a;
+      if (k < nM) {
+        kind = 2;
+        layer = s;
+        break;
+      }
+      k -= nM;
+      if (k < v) {
+        kind = 3;
+        layer = s - 1;
+        break;
+      }
+      k -= v;
+    }
+  }
+  const ChainEntry &L = ca.table[layer];
+  char *base = L.ws;
+  const WsPtrs w = chain_ws(ca, base);
+  const Outs o{L.o_approx, L.lse_approx, L.o_exact, L.lse_exact, L.ratio,
+               L.commit,   L.o_committed, ca.lambda};
+  if (kind == 0) {
+    chain_wait(chain_count(ca, layer, kCntA), nA, err);
+    approx_merge<D, G, true>(pa, w, o, k / pa.Hkv, k % pa.Hkv);
+    chain_signal(chain_count(ca, layer, kCntG));
+  } else if (kind != 3) {
+    // the layer's workspace is free once the layer before on it is done
+    if (L.prev >= 0) chain_wait(chain_count(ca, L.prev, kCntV), nV, err);
+    const bool approx = kind == 1;
+    const Item it = decode_item(pa, approx, k);
+    const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * pa.L_cap * D;
+    const int h0 = it.g * G;
+    split_any<KV, D, G, true>(L.q + ((size_t)it.b * Hq + h0) * D,
+                              (const E *)L.k + kv_off,
+                              (const E *)L.v + kv_off, it.t0, it.t1, sm_log2,
+                              w.part_ml + (size_t)it.slot * Hq + h0,
+                              w.part_acc + ((size_t)it.slot * Hq + h0) * D);
+    chain_signal(chain_count(ca, layer, approx ? kCntA : kCntM));
+  } else {
+    chain_wait(chain_count(ca, layer, kCntM), nM, err);
+    chain_wait(chain_count(ca, layer, kCntG), nG, err);
+    if (pa.NHv == 4)
+      verify_block_co<D, 4>(pa, w, o, k);
+    else if (pa.NHv == 2)
+      verify_block_co<D, 2>(pa, w, o, k);
+    else
+      verify_block_co<D, 1>(pa, w, o, k);
+    chain_signal(chain_count(ca, layer, kCntV));
+  }
+  // The last block to finish resets the control block.  Every block has
+  // taken its item (and left its waits) by then.
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(
+        chain_line(ca, 1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x - 1) {
+      __hip_atomic_store(chain_line(ca, 0), 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(chain_line(ca, 1), 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < n; ++j)
+        for (int c = 0; c < 32; c += 8)
+          __hip_atomic_store(chain_line(ca, 3 + j) + c, 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Entries of the layer table per launch of the table writer (kernel
+// arguments).
+constexpr int kChainTableChunk = 40;
+struct ChainTableChunk {
+  ChainEntry *dst;
+  int n;
+  ChainEntry e[kChainTableChunk];
+};
+
+__global__ void chain_table_kernel(ChainTableChunk c) {
+  if ((int)threadIdx.x < c.n) c.dst[threadIdx.x] = c.e[threadIdx.x];
 }
 
 // Second stage of the exact output from every split state of the plan:
@@ -1623,7 +1887,56 @@ hipError_t chain_g(const PlanArgs &pa, const ChainLayer *mid,
   return hipErrorInvalidValue;
 }
 
+template <class KV, int D, int G>
+hipError_t one_chain_kg(const PlanArgs &pa, const OneChainArgs &ca,
+                        float sm_log2, hipStream_t s) {
+  return launch(one_chain_kernel<KV, D, G>,
+                dim3(one_chain_items(pa, ca.n)), dim3(kThreads), s, pa, ca,
+                sm_log2);
+}
+
+template <class KV, int D>
+hipError_t one_chain_g(const PlanArgs &pa, const OneChainArgs &ca,
+                       float sm_log2, hipStream_t s) {
+  switch (pa.G) {
+    case 1:
+      return one_chain_kg<KV, D, 1>(pa, ca, sm_log2, s);
+    case 2:
+      return one_chain_kg<KV, D, 2>(pa, ca, sm_log2, s);
+    case 4:
+      return one_chain_kg<KV, D, 4>(pa, ca, sm_log2, s);
+    case 8:
+      return one_chain_kg<KV, D, 8>(pa, ca, sm_log2, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_one_chain(const PlanArgs &pa, int kv_dtype,
+                            const OneChainArgs &ca, float sm_log2,
+                            hipStream_t s) {
+  if (kv_dtype == ALSPEC_KV_BF16) {
+    if (pa.D == 128) return one_chain_g<KvBf16, 128>(pa, ca, sm_log2, s);
+    return one_chain_g<KvBf16, 64>(pa, ca, sm_log2, s);
+  }
+  if (pa.D == 128) return one_chain_g<KvF32, 128>(pa, ca, sm_log2, s);
+  return one_chain_g<KvF32, 64>(pa, ca, sm_log2, s);
+}
+
+hipError_t launch_chain_table(const ChainEntry *src, int n, ChainEntry *dst,
+                              hipStream_t s) {
+  for (int i = 0; i < n; i += kChainTableChunk) {
+    ChainTableChunk c;
+    c.dst = dst + i;
+    c.n = n - i < kChainTableChunk ? n - i : kChainTableChunk;
+    for (int j = 0; j < c.n; ++j) c.e[j] = src[i + j];
+    const hipError_t e =
+        launch(chain_table_kernel, dim3(1), dim3(64), s, c);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_chain(const PlanArgs &pa, int kv_dtype,
                         const ChainLayer *mid, const ChainLayer *app,

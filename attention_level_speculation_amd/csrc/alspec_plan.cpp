@@ -163,6 +163,10 @@ alspec_status make_plan(const alspec_params *p, PlanArgs *pa, Workspace *ws) {
   off = align_up(off + (size_t)B * Hq * D * 4, kWsAlign);
   ws->off_headnd = off;
   off = align_up(off + (size_t)B * Hq * 8, kWsAlign);
+  ws->off_chain_ctl = off;
+  off = align_up(off + kChainCtlBytes, kWsAlign);
+  ws->off_chain_table = off;
+  off = align_up(off + kChainMaxLayers * kChainEntryBytes, kWsAlign);
   ws->total = off;
   return ALSPEC_OK;
 }

@@ -26,6 +26,15 @@ constexpr int kUserCounters = 0;
 constexpr int kApproxCounters = kUserCounters + kMaxBatch * kCounterStride;
 constexpr int kNumCounters =
     kApproxCounters + kMaxBatch * kMaxKvHeads * kCounterStride;
+// The one-launch chain (alspec_spec_decode_layers) keeps a control block in
+// the workspace of the chain's first layer (every workspace has room for
+// one): the queue, finished and error counters (a 128-byte line each), one
+// line per layer with its counts of finished sink/window splits, middle
+// splits, merges and verifies (words 0, 8, 16 and 24 of the line), and the
+// table of the layers' buffers.  One launch covers up to kChainMaxLayers
+// layers.
+constexpr int kChainMaxLayers = 256;
+constexpr size_t kChainCtlBytes = (size_t)(3 + kChainMaxLayers) * 128;
 constexpr size_t kCounterBytes = (kNumCounters * 4 + 255) / 256 * 256;
 
 // Everything a kernel needs to map a block index to its work; passed by
@@ -49,8 +58,11 @@ struct PlanArgs {
 
 struct Workspace {
   size_t off_counters, off_part_ml, off_part_acc, off_stA_ml, off_stA_acc,
-      off_headnd, total;
+      off_headnd, off_chain_ctl, off_chain_table, total;
 };
+
+// Bytes of one entry of the one-launch chain's layer table.
+constexpr size_t kChainEntryBytes = 96;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -122,9 +122,13 @@ def parse_args():
     ap.add_argument("--ws-ring", type=int, default=0,
                     help="workspaces the eager pipelined schedule cycles "
                          "through (0: one per layer)")
+    ap.add_argument("--chain-ring", type=int, default=6,
+                    help="workspaces the layer-pipelined chains cycle "
+                         "through (at least 3; from 4 on no layer's splits "
+                         "wait for an earlier layer's verify)")
     ap.add_argument("--schedules",
                     default="pipe,pipe1,seq,pipe_eager,chain,chain_graph,"
-                            "exact,sink,fixsink",
+                            "chainL,chainL_graph,exact,sink,fixsink",
                     help="schedules to time (the fastest is the headline)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the instrumented runs (per-layer latencies)")
@@ -203,9 +207,13 @@ def main():
     # approximation and no verify
     modes = {"pipe": (2, True), "pipe1": (1, True), "seq": (0, True),
              "pipe_eager": (2, False), "chain": (None, False),
-             "chain_graph": (None, True), "exact": (None, True),
+             "chain_graph": (None, True), "chainL": (None, False),
+             "chainL_graph": (None, True), "exact": (None, True),
              "sink": (None, True), "fixsink": (None, True)}
     P = {m: params(ov or 0) for m, (ov, _) in modes.items()}
+    # the layer-pipelined chain in one launch per layer
+    P["chainL"] = params(1)
+    P["chainL_graph"] = params(1)
     splits, (T, Tw) = al.plan_splits(P["seq"], 0)
     n_mid = sum(1 for s in splits if s[0] == 2)
     mid_tokens = sum(e - b for k, b, e in splits if k == 2)
@@ -218,8 +226,12 @@ def main():
     # reuses one; each captured pipelined layer gets its own (the library
     # adds no workspace ordering under capture); the eager pipelined
     # schedule cycles through a ring, ordered by the library
+    if args.chain_ring < al.LAYERS_WS_RING:
+        raise SystemExit(f"--chain-ring must be at least {al.LAYERS_WS_RING}")
+    ring = min(nl, args.chain_ring)
     n_ws = {"seq": 1, "pipe": nl, "pipe1": nl,
-            "pipe_eager": args.ws_ring or nl, "chain": 3, "chain_graph": 3,
+            "pipe_eager": args.ws_ring or nl, "chain": ring,
+            "chain_graph": ring, "chainL": ring, "chainL_graph": ring,
             "exact": 1, "sink": 1, "fixsink": 1}
     WS = {m: [al.alloc_workspace(P[m], dev) for _ in range(n_ws[m])]
           for m in modes}
@@ -264,9 +276,9 @@ def main():
 
     # layer-pipelined chains: one alspec_layer array per (schedule, density)
     AC = {m: [B_.layers_struct(P[m], [
-        (Qs[di][l], Ks[di][l], Vs[di][l], outs[di][l], WS[m][l % 3])
+        (Qs[di][l], Ks[di][l], Vs[di][l], outs[di][l], WS[m][l % len(WS[m])])
         for l in range(nl)]) for di in range(nd)]
-        for m in ("chain", "chain_graph")}
+        for m in ("chain", "chain_graph", "chainL", "chainL_graph")}
 
     def new_events():
         evs = {n: torch.cuda.Event(enable_timing=True) for n in EVENT_NAMES}
@@ -302,7 +314,7 @@ def main():
                 if st != 0:
                     raise al.AlspecError(st, "exact-only baseline")
             return
-        if mode in ("chain", "chain_graph"):
+        if mode in ("chain", "chain_graph", "chainL", "chainL_graph"):
             st = B_._spec_decode_layers(h.ptr, ctypes.byref(P[mode]), nl,
                                         AC[mode][di], se.cuda_stream)
             if st != 0:
@@ -390,6 +402,8 @@ def main():
                       ("pipe_eager", "pipelined_eager"),
                       ("chain", "layer_pipelined"),
                       ("chain_graph", "layer_pipelined_graph"),
+                      ("chainL", "layer_pipelined_per_layer_launch"),
+                      ("chainL_graph", "layer_pipelined_per_layer_launch_graph"),
                       ("exact", "exact_only_baseline"),
                       ("sink", "static_sink_baseline"),
                       ("fixsink", "fixed_layer_sink_baseline")):
@@ -577,21 +591,38 @@ def main():
             "launch_us_mean": us,
             "launches_timed": args.kernel_launches,
         }
-        if best in ("layer_pipelined", "layer_pipelined_graph"):
-            cus, reps = chain_timing(args, B_, h, P["chain"], AC["chain"], se,
-                                     nl)
-            achieved = layer_bytes / (cus * 1e-6) / 1e9
+        if best.startswith("layer_pipelined"):
+            key = "chainL" if "per_layer_launch" in best else "chain"
+            lus, cus, group, reps = chain_timing(args, B_, h, P[key], AC[key],
+                                                 se, nl)
+            if group > 1:
+                # the whole chain is one launch: its bytes over its duration
+                achieved = layer_bytes * group / (cus * 1e-6) / 1e9
+                kern = ("one_chain_kernel<KvBf16,128,4> (the whole chain of "
+                        f"{group} layers in one launch, items taken from a "
+                        "queue: merges of sink and window states, sink and "
+                        "window splits of the next layer, middle splits, "
+                        "verifies of the layer before; the launch time "
+                        "includes the layer-table writer before it)")
+            else:
+                achieved = layer_bytes / (lus * 1e-6) / 1e9
+                kern = ("chain_kernel<KvBf16,128,4> (steady state: merge of "
+                        "layer j's approximation, middle splits of layer j, "
+                        "sink and window splits of layer j+1, verify of "
+                        "layer j-1)")
             out["roofline"] = {
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                "traffic": measured_traffic("chain"),
-                "kernel": "chain_kernel<KvBf16,128,4> (steady state: "
-                          "merge of layer j's approximation, middle splits "
-                          "of layer j, sink and window splits of layer j+1, "
-                          "verify of layer j-1)",
-                "algorithmic_bytes_per_launch": layer_bytes,
+                "traffic": measured_traffic("one_chain" if group > 1
+                                            else "chain"),
+                "kernel": kern,
+                "algorithmic_bytes_per_launch": layer_bytes * group,
                 "launch_us_mean": cus,
-                "launches_timed": reps * nd * (nl - 2),
+                "layers_per_launch": group,
+                "us_per_layer_steady": lus,
+                "steady_frac": layer_bytes / (lus * 1e-6) / 1e9 /
+                HBM_PEAK_GBPS,
+                "chains_timed": reps * nd,
             }
             out["roofline_exact_pass"] = exact_pass
         else:
@@ -712,10 +743,12 @@ def projection(seq, exact_only_us, post_us, hit):
 
 def config_records(args, al, B_, h, dev, which):
     """The other configurations as layer-pipelined chains
-    (alspec_spec_decode_layers), one at a time, each drawn on the device and
+    (alspec_spec_decode_layers) in both its forms (one launch; one launch
+    per layer), one configuration at a time, each drawn on the device and
     freed after: the chain's wall time per decode token (HIP events around
-    back-to-back chains of all layers), its steady launch against the HBM
-    roofline (as for the headline), and the hit rate."""
+    back-to-back chains of all layers), its launch against the HBM roofline
+    (as for the headline), and the hit rate; the faster form is the
+    record's."""
     import torch
 
     from synth import device as sdev
@@ -736,51 +769,82 @@ def config_records(args, al, B_, h, dev, which):
         torch.cuda.synchronize()
         log(f"{name}: drew {nl} layers ({2 * K.numel() * 2 / 2**30:.1f} GiB) "
             f"t={time.time() - t0:.1f}s")
-        p = al.params_for(w)
-        wss = [al.alloc_workspace(p, dev) for _ in range(3)]
-        outs = [al.alloc_outputs(p, dev) for _ in range(nl)]
-        arr = B_.layers_struct(p, [(Q[l], K[l], V[l], outs[l], wss[l % 3])
-                                   for l in range(nl)])
-        s = torch.cuda.Stream(device=dev)
-        steady, reps = chain_timing(args, B_, h, p, [arr], s, nl)
-        # whole chains, back to back
-        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-        torch.cuda.synchronize()
-        e0.record(s)
-        for _ in range(reps):
-            st = B_._spec_decode_layers(h.ptr, ctypes.byref(p), nl, arr,
-                                        s.cuda_stream)
-            if st != 0:
-                raise al.AlspecError(st, "alspec_spec_decode_layers")
-        e1.record(s)
-        torch.cuda.synchronize()
-        chain_us = e0.elapsed_time(e1) * 1e3 / reps
         layer_bytes = sum(w.seq_lens) * w.Hkv * w.D * 2 * 2
-        ratio = torch.stack([o["ratio"] for o in outs]).cpu().numpy()
-        achieved = layer_bytes / (steady * 1e-6) / 1e9
+        s = torch.cuda.Stream(device=dev)
+        forms = {}
+        for form, overlap in (("one_launch", 0), ("per_layer_launch", 1)):
+            p = al.params_for(w, overlap=overlap)
+            wss = [al.alloc_workspace(p, dev)
+                   for _ in range(min(nl, args.chain_ring))]
+            outs = [al.alloc_outputs(p, dev) for _ in range(nl)]
+            arr = B_.layers_struct(p, [(Q[l], K[l], V[l], outs[l],
+                                        wss[l % len(wss)])
+                                       for l in range(nl)])
+            steady, launch_us, group, reps = chain_timing(args, B_, h, p,
+                                                          [arr], s, nl)
+            # whole chains, back to back
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                st = B_._spec_decode_layers(h.ptr, ctypes.byref(p), nl, arr,
+                                            s.cuda_stream)
+                if st != 0:
+                    raise al.AlspecError(st, "alspec_spec_decode_layers")
+            e1.record(s)
+            torch.cuda.synchronize()
+            chain_us = e0.elapsed_time(e1) * 1e3 / reps
+            # the launch's bytes over its duration (one launch: the whole
+            # chain; one launch per layer: a steady layer)
+            achieved = layer_bytes * group / (launch_us * 1e-6) / 1e9
+            kern = ("one_chain_kernel (the whole chain of "
+                    f"{group} layers in one launch)" if group > 1 else
+                    "chain_kernel (one launch per layer, steady state)")
+            forms[form] = {
+                "tokens_layers_per_s": w.B * nl / (chain_us * 1e-6),
+                "us_per_layer": chain_us / nl,
+                "chains_timed": reps,
+                "roofline": {"bound": "hbm", "achieved": achieved,
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBPS,
+                             "traffic": None, "kernel": kern,
+                             "algorithmic_bytes_per_launch":
+                                 layer_bytes * group,
+                             "launch_us_mean": launch_us,
+                             "layers_per_launch": group,
+                             "us_per_layer_steady": steady,
+                             "steady_frac": layer_bytes / (steady * 1e-6) /
+                             1e9 / HBM_PEAK_GBPS},
+                "ratio": torch.stack([o["ratio"] for o in outs]).cpu()
+                .numpy(),
+            }
+            log(f"{name} {form}: {chain_us / nl:.1f} us per layer "
+                f"({achieved / HBM_PEAK_GBPS:.3f} of peak per launch), "
+                f"steady {steady:.1f} us per layer")
+            del outs, wss, arr
+        best = min(forms, key=lambda f: forms[f]["us_per_layer"])
+        ratio = forms[best].pop("ratio")
+        for f in forms.values():
+            f.pop("ratio", None)
         lams = (0.05, 0.10, 0.20) if name == "c4" else (w.lam,)
         recs[name] = {
             "workload": f"{w.name}: batch {w.B}, {w.Hq} q / {w.Hkv} kv heads, "
                         f"head dim {w.D}, bf16 KV, context "
                         f"{min(w.seq_lens)}-{max(w.seq_lens)}, sink {w.S}, "
                         f"window {w.W}, {nl} layers",
-            "schedule": "layer_pipelined (alspec_spec_decode_layers, "
-                        "eager, one call per decode token)",
-            "tokens_layers_per_s": w.B * nl / (chain_us * 1e-6),
-            "us_per_layer": chain_us / nl,
-            "chains_timed": reps,
-            "roofline": {"bound": "hbm", "achieved": achieved,
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                         "kernel": "chain_kernel (steady state)",
-                         "algorithmic_bytes_per_launch": layer_bytes,
-                         "launch_us_mean": steady},
+            "schedule": f"layer_pipelined, {best} (alspec_spec_decode_layers,"
+                        " eager, one call per decode token; the faster of "
+                        "its two forms)",
+            "workspaces": min(nl, args.chain_ring),
+            "tokens_layers_per_s": forms[best]["tokens_layers_per_s"],
+            "us_per_layer": forms[best]["us_per_layer"],
+            "chains_timed": forms[best]["chains_timed"],
+            "roofline": forms[best]["roofline"],
+            "forms": forms,
             "hit_rate": {str(lam): float((ratio <= lam).mean())
                          for lam in lams},
         }
-        log(f"{name}: {recs[name]['us_per_layer']:.1f} us per layer, steady "
-            f"launch {steady:.1f} us ({achieved / HBM_PEAK_GBPS:.3f} of peak)")
-        del K, V, Q, outs, wss, arr
+        del K, V, Q
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return recs
@@ -954,19 +1018,23 @@ def kernel_timing(args, al, B_, h, p, Qs, Ks, Vs, stream, nd, nl):
 
 
 def chain_timing(args, B_, h, p, arrs, stream, nl):
-    """Average duration of the layer-pipelined kernel in its steady state
-    (approximation of layer j+1, middle splits of layer j, verify of layer
-    j-1 in one launch).  alspec_spec_decode_layers runs back to back over
-    all nl layers and, separately, over the first two, each bracketed by
-    two HIP events on the stream it runs on; both hold one first and one
-    last launch plus the chain's lone first approximation and last verify,
-    so the difference of the two per-call times over nl - 2 is one
-    steady-state launch (inter-launch gaps count against it).  Returns
-    (microseconds, repetitions per density)."""
+    """Device time of the layer-pipelined chain: per call and per layer in
+    its steady state.  alspec_spec_decode_layers runs back to back over all
+    nl layers and, separately, over the first short_n, each bracketed by two
+    HIP events on the stream it runs on; both calls hold the chain's first
+    approximation and its last verify, so the difference of the two per-call
+    times is nl - short_n steady layers (inter-launch gaps count against
+    it).  In one launch (p.overlap 0) the per-call time is the launch's
+    (with the small table writer before it) and short_n is nl / 2; in one
+    launch per layer (p.overlap 1) short_n is 2 and the per-launch time is
+    the per-layer one.  Returns (microseconds per steady layer,
+    microseconds per launch, layers per launch, repetitions per density)."""
     import torch
     if nl < 3:
-        raise SystemExit("the chain's steady state needs at least 3 layers")
-    two = [(B_.Layer * 2)(a[0], a[1]) for a in arrs]
+        raise SystemExit("the steady state needs at least 3 layers")
+    short_n = nl // 2 if p.overlap == 0 else 2
+    span = nl - short_n
+    short = [(B_.Layer * short_n)(*a[:short_n]) for a in arrs]
 
     def run(layers, n, reps):
         for _ in range(reps):
@@ -983,13 +1051,16 @@ def chain_timing(args, B_, h, p, arrs, stream, nl):
     run(arrs, nl, reps)
     ev[1].record(stream)
     ev[2].record(stream)
-    run(two, 2, reps)
+    run(short, short_n, reps)
     ev[3].record(stream)
     torch.cuda.synchronize()
     n = reps * len(arrs)
     full = ev[0].elapsed_time(ev[1]) * 1e3 / n
-    short = ev[2].elapsed_time(ev[3]) * 1e3 / n
-    return (full - short) / (nl - 2), reps
+    part = ev[2].elapsed_time(ev[3]) * 1e3 / n
+    per_layer = (full - part) / span
+    if p.overlap == 0:
+        return per_layer, full, nl, reps
+    return per_layer, per_layer, 1, reps
 
 
 def cpu_baseline(args, works, dens, outs, nl, Qs, Ks, Vs):

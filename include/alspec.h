@@ -326,33 +326,50 @@ typedef struct {
   size_t ws_bytes;
 } alspec_layer;
 
+/* Workspaces of alspec_spec_decode_layers: layers fewer than this many
+ * apart in one call must not share a workspace (either form), so a ring of
+ * this many workspaces serves any chain. */
+#define ALSPEC_LAYERS_WS_RING 3
+
 /*
  * The fused step for a chain of n_layers layers of one decode step, on one
  * stream, layer-pipelined: the speculative order of "Attention-Level
  * Speculation" (atlas.scime.ai research-map page, summary and Approach:
  * downstream work starts on the approximation while exact attention is
  * still running), for layers whose queries are all given (independent
- * layers).  Launch 0 computes layer 0's approximation; launch j (j =
- * 0..n-1) computes, in disjoint block ranges of one grid, the merge of
- * layer j's sink and window states into its approximate output (for j >=
- * 1; these blocks are dispatched first), layer j's middle splits, layer
- * j+1's sink and window splits, and layer j-1's exact merge, verify and
- * commit; a last launch verifies layer n-1.  So layer j's approximate
- * output is complete a few microseconds into launch j and its exact
- * output and verdict in launch j+1.  Stream order alone carries the
- * dependencies, so successive exact passes run back to back with no
- * event, cross-stream wait or device-scope hand-off between them.  A
- * stack whose next query is computed from the approximate output runs
- * through the single-layer calls instead.  Each layer's outputs equal
- * those of alspec_spec_decode (any mode) on its inputs, bit for bit.
- * p->overlap is ignored.
+ * layers).  Each layer's outputs equal those of alspec_spec_decode (any
+ * mode) on its inputs, bit for bit.
  *
- * `layers` is a host array of n_layers entries (>= 1), each validated as
- * the arguments of alspec_spec_decode.  Entries whose layers are fewer
- * than 3 apart must not share a workspace (ALSPEC_ERR_WORKSPACE); from 3
- * apart they may (a ring of three workspaces serves any chain).  Calls
- * sharing a workspace with other calls are ordered by the caller.  May be
- * captured into a HIP graph.
+ * p->overlap == 0 (default), one launch: a small kernel first writes the
+ * table of the layers' buffers into the first layer's workspace; then one
+ * launch runs the whole chain, its blocks taking work items, one each,
+ * from a queue in that workspace: the first layer's sink and window
+ * splits, then for each layer j in turn the merge of layer j's sink and
+ * window states into its approximate output, layer j+1's sink and window
+ * splits, layer j's middle splits and layer j-1's exact merge, verify and
+ * commit, and last the last layer's verify.  A block takes the next item
+ * when it starts, so faster compute units take more items, one layer's
+ * slowest blocks do not delay the next layer's, and the launch's tail is
+ * paid once per call.  Items that need others' results wait on per-layer
+ * completion counts, and a layer's splits wait for the verify of the
+ * latest earlier layer on the same workspace; every wait is bounded (one
+ * that runs out leaves that layer's outputs wrong and counts itself in
+ * the workspace; it does not hang).  Chains longer than 256 layers take
+ * one such pair of launches per 256 layers.
+ *
+ * p->overlap == 1, one launch per layer: launch j computes, in disjoint
+ * block ranges of one grid, the merge of layer j's sink and window states
+ * (for j >= 1; dispatched first), layer j's middle splits, layer j+1's sink
+ * and window splits, and layer j-1's exact merge, verify and commit; a last
+ * launch verifies layer n-1.  Stream order alone carries the dependencies.
+ *
+ * A stack whose next query is computed from the approximate output runs
+ * through the single-layer calls instead.  `layers` is a host array of
+ * n_layers entries (>= 1), each validated as the arguments of
+ * alspec_spec_decode; layers fewer than ALSPEC_LAYERS_WS_RING apart that
+ * share a workspace return ALSPEC_ERR_WORKSPACE with nothing enqueued.
+ * Calls sharing a workspace with other calls are ordered by the caller.
+ * May be captured into a HIP graph.
  */
 alspec_status alspec_spec_decode_layers(alspec_handle *h,
                                         const alspec_params *p,

@@ -507,9 +507,11 @@ def test_half_captured_call_rejected(handle):
     assert x.tolist() == [1.0] * 4
 
 
-def _chain(handle, w, n_layers, n_ws=3, lam=None):
+def _chain(handle, w, n_layers, n_ws=None, lam=None, overlap=0):
     lam = w.lam if lam is None else lam
-    p = al.params_for(w, lam=lam)
+    p = al.params_for(w, lam=lam, overlap=overlap)
+    if n_ws is None:
+        n_ws = al.LAYERS_WS_RING
     devs = [to_device(*gen.layer_inputs(w, l)) for l in range(n_layers)]
     wss = [al.alloc_workspace(p) for _ in range(n_ws)]
     outs = [al.alloc_outputs(p) for _ in range(n_layers)]
@@ -526,16 +528,21 @@ def _single_with_chain_plan(p):
     return q
 
 
+@pytest.mark.parametrize("overlap", [0, 1])
 @pytest.mark.parametrize("shape,n_layers", [
     ("bf16_g4", 1), ("bf16_g4", 2), ("bf16_g4", 5), ("f32_g2", 4),
     ("bf16_g8_ragged", 3), ("f32_d64_g1_ragged", 4),
-    ("bf16_d64_g4_tiny", 3)])
-def test_layers_chain_matches_single_calls(handle, shape, n_layers):
-    """The layer-pipelined chain gives every layer exactly the outputs of a
-    single fused call on its inputs with the same plan, with a ring of three
-    workspaces (each sized for the single calls' automatic plan): MFMA
-    and VALU split kernels, head dims 128 and 64, users whose context is
-    shorter than the sink plus window (no middle) or a single token."""
+    ("bf16_d64_g4_tiny", 3), ("bf16_g4", 8), ("bf16_g4", 9),
+    ("bf16_g4", 17)])
+def test_layers_chain_matches_single_calls(handle, shape, n_layers, overlap):
+    """The layer-pipelined chain, in one launch (overlap 0: items taken
+    from a queue, layers reusing a workspace waiting for the verify three
+    layers back) and in one launch per layer (overlap 1), gives every layer
+    exactly the outputs of a single fused call on its inputs with the same
+    plan, with the smallest ring of workspaces allowed (each sized for the
+    single calls' automatic plan): MFMA and
+    VALU split kernels, head dims 128 and 64, users whose context is shorter
+    than the sink plus window (no middle) or a single token."""
     w = {"bf16_g4": gen.scaled(gen.llama8b_32k(), 6000),
          "f32_g2": _mk("c2", 2, 8, 4, 128, [2500, 777], "f32", 4, 256),
          "bf16_g8_ragged": _mk("c8", 3, 16, 2, 128, [3000, 130, 5000],
@@ -544,11 +551,12 @@ def test_layers_chain_matches_single_calls(handle, shape, n_layers):
                                   "f32", 4, 100),
          "bf16_d64_g4_tiny": _mk("c4", 4, 8, 2, 64, [1, 2049, 5, 300],
                                  "bf16", 4, 128)}[shape]
-    print(f"[case] chain {shape} layers={n_layers}", flush=True)
-    p, devs, wss, outs = _chain(handle, w, n_layers)
+    print(f"[case] chain {shape} layers={n_layers} overlap={overlap}",
+          flush=True)
+    p, devs, wss, outs = _chain(handle, w, n_layers, overlap=overlap)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3])
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)])
                                       for j, (d, o) in enumerate(zip(devs,
                                                                      outs))],
                           s)
@@ -564,6 +572,37 @@ def test_layers_chain_matches_single_calls(handle, shape, n_layers):
     ref = oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam)
     compare({k_: v_.cpu().numpy() for k_, v_ in outs[-1].items()}, ref,
             w.kv_dtype, w.lam, "chain-last")
+
+
+@pytest.mark.parametrize("pattern,n_layers", [
+    ("ring4", 11), ("irregular", 12), ("ring3", 260)])
+def test_layers_chain_workspace_patterns(handle, pattern, n_layers):
+    """The one-launch chain with workspaces reused at distances other than
+    three (a ring of four; an irregular assignment where a layer's latest
+    predecessor on its workspace lies three to five layers back) and a chain
+    longer than one launch's 256 layers: every layer bit for bit equal to a
+    single fused call on its inputs."""
+    w = _mk("wp", 4, 8, 2, 64, [1, 2049, 5, 300], "bf16", 4, 128)
+    print(f"[case] chain workspaces {pattern} layers={n_layers}", flush=True)
+    p = al.params_for(w)
+    order = {"ring4": [j % 4 for j in range(n_layers)],
+             "irregular": [0, 1, 2, 0, 3, 1, 4, 2, 0, 3, 1, 4],
+             "ring3": [j % 3 for j in range(n_layers)]}[pattern]
+    assert len(order) == n_layers
+    for j, a in enumerate(order):
+        assert a not in order[max(0, j - 2):j]
+    wss = [al.alloc_workspace(p) for _ in range(max(order) + 1)]
+    base = [to_device(*gen.layer_inputs(w, l)) for l in range(7)]
+    devs = [base[j % 7] for j in range(n_layers)]
+    outs = [al.alloc_outputs(p) for _ in range(n_layers)]
+    al.spec_decode_layers(handle, p, [(*devs[j], outs[j], wss[order[j]])
+                                      for j in range(n_layers)])
+    torch.cuda.synchronize()
+    ps = _single_with_chain_plan(p)
+    refs = [run_fused(al, handle, ps, *d) for d in base]
+    for j in range(n_layers):
+        for key, want in refs[j % 7].items():
+            assert np.array_equal(outs[j][key].cpu().numpy(), want), (j, key)
 
 
 @pytest.mark.parametrize("shape,n_layers", [("llama8b_128k", 4),
@@ -583,9 +622,9 @@ def test_layers_chain_full_size(handle, shape, n_layers):
         refs.append(oracle.spec_decode(q, k, v, w.seq_lens, w.S, w.W, w.lam))
         devs.append(to_device(q, k, v))
         del q, k, v
-    wss = [al.alloc_workspace(p) for _ in range(3)]
+    wss = [al.alloc_workspace(p) for _ in range(al.LAYERS_WS_RING)]
     outs = [al.alloc_outputs(p) for _ in range(n_layers)]
-    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)]) for j, (d, o)
                                       in enumerate(zip(devs, outs))])
     torch.cuda.synchronize()
     ps = _single_with_chain_plan(p)
@@ -604,7 +643,7 @@ def test_layers_chain_graph_replays(handle):
     w = gen.scaled(gen.llama8b_32k(), 5000)
     p, devs, wss, outs = _chain(handle, w, 4)
     eager = [al.alloc_outputs(p) for _ in devs]
-    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o) in
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)]) for j, (d, o) in
                                       enumerate(zip(devs, eager))])
     torch.cuda.synchronize()
     want = [{k_: v_.cpu().numpy() for k_, v_ in o.items()} for o in eager]
@@ -612,7 +651,7 @@ def test_layers_chain_graph_replays(handle):
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
-        al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+        al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)]) for j, (d, o)
                                           in enumerate(zip(devs, outs))],
                               cap)
     for rep in range(3):
@@ -627,6 +666,27 @@ def test_layers_chain_graph_replays(handle):
             for key in want[j]:
                 assert np.array_equal(o[key].cpu().numpy(), want[j][key]), \
                     (rep, j, key)
-        al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+        al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)]) for j, (d, o)
                                           in enumerate(zip(devs, eager))])
         torch.cuda.synchronize()
+
+
+def test_layers_ring_rule(handle):
+    """Both forms refuse layers fewer than ALSPEC_LAYERS_WS_RING (3) apart
+    on one workspace (status 3, nothing enqueued)."""
+    w = _mk("ring", 1, 8, 2, 128, [1500], "bf16", 4, 128)
+    dev = to_device(*gen.layer_inputs(w, 0))
+    assert al.LAYERS_WS_RING == 3
+    for overlap, ring, ok in ((0, 2, False), (0, 3, True),
+                              (1, 2, False), (1, 3, True)):
+        p = al.params_for(w, overlap=overlap)
+        wss = [al.alloc_workspace(p) for _ in range(ring)]
+        outs = [al.alloc_outputs(p) for _ in range(12)]
+        layers = [(*dev, o, wss[j % ring]) for j, o in enumerate(outs)]
+        if ok:
+            al.spec_decode_layers(handle, p, layers)
+            torch.cuda.synchronize()
+        else:
+            with pytest.raises(al.AlspecError) as e:
+                al.spec_decode_layers(handle, p, layers)
+            assert e.value.status == 3

@@ -77,7 +77,7 @@ def test_random_shape(handle, i):
         return
     wss = [al.alloc_workspace(p) for _ in range(3)]
     outs = [al.alloc_outputs(p) for _ in range(n_layers)]
-    al.spec_decode_layers(handle, p, [(*d, o, wss[j % 3]) for j, (d, o)
+    al.spec_decode_layers(handle, p, [(*d, o, wss[j % len(wss)]) for j, (d, o)
                                       in enumerate(zip(devs, outs))])
     torch.cuda.synchronize()
     ps = type(p).from_buffer_copy(p)
