@@ -665,6 +665,9 @@ def main():
         torch.cuda.empty_cache()
         pr = sdev.probe_bandwidth()
         out["probe"] = {k: round(v["GBps"], 1) for k, v in pr.items()}
+        out["probe"]["read_settings"] = {
+            k: pr["read"][k] for k in ("blocks", "loads_in_flight",
+                                       "nontemporal")}
         for key in ("roofline", "roofline_exact_pass"):
             if key in out:
                 out[key]["frac_of_probe_read"] = (
@@ -850,6 +853,13 @@ def config_records(args, al, B_, h, dev, which):
     return recs
 
 
+def B_params_seq(al, p):
+    """p with the sequential overlap mode (the chained step's)."""
+    q = type(p).from_buffer_copy(p)
+    q.overlap = 0
+    return q
+
+
 def model_timing(args, al, h, w, Q, K, V, nl, dev):
     """One decode token through nl Llama-3-8B-shaped layers: the attention
     step on the resident 128K KV, then the post-attention operators with
@@ -972,6 +982,53 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
         return {"us_per_layer": wall * 1e6 / nl,
                 "tokens_layers_per_s": nl / wall,
                 "commit_rate": sum(commits) / nl}
+    # the approximation against the exact pass inside the model step: the
+    # one-stream speculative order (approximation, post-attention on it,
+    # exact pass and merge, verify, post-attention replay where discarded),
+    # HIP events around the approximation and around the exact pass of
+    # every layer
+    p = al.params_for(w)
+    p0 = B_params_seq(al, p)
+    outs = [al.alloc_outputs(p0, dev) for _ in range(nl)]
+    ws = al.alloc_workspace(p0, dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+          for _ in range(nl)]
+    t_a, t_e = [], []
+    for it in range(1 + args.model_steps):
+        torch.cuda.synchronize()
+        q = Q[0]
+        for l in range(nl):
+            o = outs[l]
+            ev[l][0].record(se)
+            al.sink_approx(h, p0, q, K[l], V[l], o["o_approx"],
+                           o["lse_approx"], ws, se)
+            ev[l][1].record(se)
+            al.post_attention(h, pp, structs[l], o["o_approx"].view(1, -1),
+                              hs[l], hs[l + 1], qkvs[l], wsp[0], stream=se)
+            ev[l][2].record(se)
+            al.flash_decode_exact(h, p0, q, K[l], V[l], 0, ws, se)
+            al.lse_combine(h, p0, ws, o["o_exact"], o["lse_exact"], se)
+            ev[l][3].record(se)
+            al.verify(h, p0, o["o_approx"], o["o_exact"], o["ratio"],
+                      o["commit"], o["o_committed"], se)
+            al.post_attention(h, pp, structs[l], o["o_exact"].view(1, -1),
+                              hs[l], hs[l + 1], qkvs[l], wsp[1],
+                              skip=o["commit"], stream=se)
+            q = rt.q_view(p0, qkvs[l])
+        torch.cuda.synchronize()
+        if it:  # the first token warms up
+            for l in range(nl):
+                t_a.append(ev[l][0].elapsed_time(ev[l][1]) * 1e3)
+                t_e.append(ev[l][2].elapsed_time(ev[l][3]) * 1e3)
+    ta, te = sum(t_a) / len(t_a), sum(t_e) / len(t_e)
+    res["attention_split"] = {
+        "measure": "HIP events around the approximation call and around "
+                   "the exact pass (split-K over the middle and merge) of "
+                   "every layer, in the one-stream speculative order with "
+                   "the post-attention work between them",
+        "approx_us_mean": ta, "exact_us_mean": te,
+        "approx_over_exact": ta / te, "layers_timed": len(t_a)}
+    del outs, ws
     res["exact_only"] = run(w.lam, exact_only=True)
     res["exact_only"].pop("commit_rate")
     res["spec_sequence"] = run(w.lam, speculative=False)

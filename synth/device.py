@@ -86,6 +86,7 @@ def _probe_lib():
         lib.probe_read.restype = ctypes.c_int
         lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p]
         lib.probe_copy.restype = ctypes.c_int
         lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
@@ -95,27 +96,27 @@ def _probe_lib():
     return lib
 
 
+PROBE_READ_BLOCKS = (1024, 2048, 4096, 8192)
+PROBE_READ_UNROLL = (1, 2, 4, 8)
+
+
 def probe_bandwidth(nbytes=4 << 30, reps=10, blocks=256 * 16):
     """Achievable read and copy bandwidth (GB/s, 1e9 bytes) over `nbytes`
-    buffers, timed with HIP events; each kernel averaged over `reps`."""
+    buffers, timed with HIP events; each kernel averaged over `reps`.  The
+    read is swept over grid sizes, loads in flight per thread and plain or
+    nontemporal loads; "read" is the fastest of the sweep (its settings
+    beside it), "read_simple" one nontemporal load per thread on `blocks`
+    blocks; the copy runs on `blocks` blocks."""
     import torch
     lib = _probe_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
-    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(max(PROBE_READ_BLOCKS + (blocks,)), dtype=torch.int32,
+                       device="cuda")
     s = torch.cuda.current_stream()
-    res = {}
-    for name in ("read", "copy"):
-        def launch():
-            if name == "read":
-                rc = lib.probe_read(src.data_ptr(), nbytes, sink.data_ptr(),
-                                    blocks, s.cuda_stream)
-            else:
-                rc = lib.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes,
-                                    blocks, s.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"probe_{name} failed: {rc}")
+
+    def timed(launch, moved):
         launch()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -125,8 +126,28 @@ def probe_bandwidth(nbytes=4 << 30, reps=10, blocks=256 * 16):
         e1.record(s)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        moved = nbytes * (1 if name == "read" else 2)
-        res[name] = {"bytes_per_launch": moved, "ms": ms,
-                     "GBps": moved / (ms * 1e-3) / 1e9}
+        return {"bytes_per_launch": moved, "ms": ms,
+                "GBps": moved / (ms * 1e-3) / 1e9}
+
+    def read(nb, unroll, nt):
+        def launch():
+            rc = lib.probe_read(src.data_ptr(), nbytes, sink.data_ptr(), nb,
+                                unroll, nt, s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe_read failed: {rc}")
+        r = timed(launch, nbytes)
+        r.update(blocks=nb, loads_in_flight=unroll, nontemporal=bool(nt))
+        return r
+
+    def copy():
+        rc = lib.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks,
+                            s.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_copy failed: {rc}")
+    sweep = [read(nb, u, nt) for nb in PROBE_READ_BLOCKS
+             for u in PROBE_READ_UNROLL for nt in (0, 1)]
+    res = {"read": max(sweep, key=lambda r: r["GBps"]),
+           "read_simple": read(blocks, 1, 1),
+           "copy": timed(copy, 2 * nbytes)}
     del src, dst, sink
     return res

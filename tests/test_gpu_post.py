@@ -65,6 +65,12 @@ SHAPES = [
     # of the 4-row wave tile or the 16-row block), short and long K
     ("ragged_small", 3, 40, 48, 136, 20),
     ("one_row_tails", 1, 8, 8, 8, 1),
+    # one and two entries (the split-K forms of the gated MLP and the down
+    # projection): ragged row blocks, K shorter than the four waves'
+    # shares, long K
+    ("b2_ragged", 2, 40, 48, 136, 20),
+    ("b1_k_tail", 1, 520, 1032, 2056, 77),
+    ("b2_long_k", 2, 256, 264, 14344, 9),
     ("k_tail", 2, 520, 1032, 2056, 77),
     ("max_batch", 8, 256, 512, 1024, 384),
     ("mid_70b_like", 4, 1024, 2048, 5632, 3072),
@@ -144,3 +150,53 @@ def test_in_place_residual(handle):
                       al.alloc_post_workspace(p))
     torch.cuda.synchronize()
     assert torch.equal(hd, ref_h) and torch.equal(qkv, ref_q)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_small_batch_repeats_and_skips(handle, B):
+    """One or two entries (the decode step's batch) on one workspace: five
+    calls in a row give identical bits, skip flags leave flagged entries
+    untouched and the others equal to the unflagged call, and all entries
+    flagged leaves everything as it was."""
+    s = pg.PostShape("small_batch", B, 72, 136, 1000, 40, seed=11 + B)
+    print(f"[case] post small batch B={B}", flush=True)
+    w = pg.weights(s)
+    wd = _dev_weights(s, w)
+    o, h = pg.activations(s)
+    p = al.make_post_params(s.B, s.attn_dim, s.hidden, s.ffn, s.qkv_dim,
+                            s.eps)
+    ws = al.alloc_post_workspace(p)
+    od = torch.from_numpy(o).cuda()
+    hd = torch.from_numpy(h).cuda()
+
+    def call(skip=None, h0=None, q0=None):
+        h_out = (torch.full((s.B, s.hidden), float("nan"), device="cuda")
+                 if h0 is None else h0.clone())
+        qkv = (torch.full((s.B, s.qkv_dim), float("nan"), device="cuda")
+               if q0 is None else q0.clone())
+        sk = None if skip is None else torch.tensor(skip, dtype=torch.uint8,
+                                                    device="cuda")
+        al.post_attention(handle, p, wd, od, hd, h_out, qkv, ws, skip=sk)
+        torch.cuda.synchronize()
+        return h_out, qkv
+    first = call()
+    ref_h, ref_q = op.post_attention(o, h, w, s.eps)
+    assert max(_rel(first[0].cpu().numpy(), ref_h)) <= BAR
+    assert max(_rel(first[1].cpu().numpy(), ref_q)) <= BAR
+    for _ in range(4):
+        again = call()
+        assert torch.equal(again[0], first[0])
+        assert torch.equal(again[1], first[1])
+    prev_h = torch.full((s.B, s.hidden), 7.0, device="cuda")
+    prev_q = torch.full((s.B, s.qkv_dim), -3.0, device="cuda")
+    patterns = [[1], [0]] if B == 1 else [[1, 0], [0, 1], [1, 1], [0, 0]]
+    for flags in patterns:
+        got_h, got_q = call(flags, prev_h, prev_q)
+        for b, f in enumerate(flags):
+            want_h = prev_h[b] if f else first[0][b]
+            want_q = prev_q[b] if f else first[1][b]
+            assert torch.equal(got_h[b], want_h), (flags, b)
+            assert torch.equal(got_q[b], want_q), (flags, b)
+    # and once more unflagged after the flagged calls
+    last = call()
+    assert torch.equal(last[0], first[0]) and torch.equal(last[1], first[1])
