@@ -89,13 +89,20 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "238379be9b2fc354771fea1027101615"
-                     "d9e2a7007d5bc2414caff6ff6717dc38",
-           # (fetch, write) per launch; the chain kernel's in its steady
-           # state (all four block ranges)
-           "bytes": {"chain": (262912.2 * 1024 * 2.0, 862.9 * 1024 * 1.0),
-                     "partials_middle": (258167.6 * 1024 * 2.0,
-                                         520.0 * 1024 * 1.0)}}
+           "sha256": "875720c9cceb848694c7a3cdb6765d95"
+                     "725beddb065692d18bb311c7ff871b76",
+           # (fetch, write) per launch: the per-layer chain kernel in its
+           # steady state (all four block ranges), the exact split-K pass,
+           # the one-launch chain of the 32 layers at 128K, and the two
+           # chain forms of the 32K configuration
+           "bytes": {"chain": (262915.4 * 1024 * 2.0, 862.5 * 1024 * 1.0),
+                     "partials_middle": (258168.6 * 1024 * 2.0,
+                                         520.0 * 1024 * 1.0),
+                     "one_chain": (8407514.5 * 1024 * 2.0,
+                                   30018.7 * 1024 * 1.0),
+                     "c2_one_chain": (2115236.9 * 1024 * 2.0,
+                                      29451.2 * 1024 * 1.0),
+                     "c2_chain": (66292.8 * 1024 * 2.0, 846.6 * 1024 * 1.0)}}
 
 
 def measured_traffic(kernel):
@@ -810,7 +817,9 @@ def config_records(args, al, B_, h, dev, which):
                 "roofline": {"bound": "hbm", "achieved": achieved,
                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": achieved / HBM_PEAK_GBPS,
-                             "traffic": None, "kernel": kern,
+                             "traffic": measured_traffic(
+                                 f"{name}_{'one_chain' if group > 1 else 'chain'}"),
+                             "kernel": kern,
                              "algorithmic_bytes_per_launch":
                                  layer_bytes * group,
                              "launch_us_mean": launch_us,
