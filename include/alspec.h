@@ -98,8 +98,9 @@ typedef struct {
                                   entry point takes the same plan, so the
                                   layered and single calls give the same
                                   bits. */
-  int32_t overlap; /* fused call only: 0 = sequential, 1 = overlapped,
-                      2 = pipelined (see alspec_spec_decode) */
+  int32_t overlap; /* 0 = sequential, 1 = overlapped, 2 = pipelined (see
+                      alspec_spec_decode); alspec_spec_decode_layers: 0 or
+                      2 = one launch per chain, 1 = one launch per layer */
 } alspec_params;
 
 #define ALSPEC_MAX_BATCH 64
@@ -340,11 +341,11 @@ typedef struct {
  * layers).  Each layer's outputs equal those of alspec_spec_decode (any
  * mode) on its inputs, bit for bit.
  *
- * p->overlap == 0 (default), one launch: a small kernel first writes the
- * table of the layers' buffers into the first layer's workspace; then one
- * launch runs the whole chain, its blocks taking work items, one each,
- * from a queue in that workspace: the first layer's sink and window
- * splits, then for each layer j in turn the merge of layer j's sink and
+ * p->overlap == 0 (default; 2 is taken as 0), one launch: a small kernel
+ * first writes the table of the layers' buffers into the first layer's
+ * workspace; then one launch runs the whole chain, its blocks taking work
+ * items, one each, from a queue in that workspace: the first layer's sink
+ * and window splits, then for each layer j in turn the merge of layer j's sink and
  * window states into its approximate output, layer j+1's sink and window
  * splits, layer j's middle splits and layer j-1's exact merge, verify and
  * commit, and last the last layer's verify.  A block takes the next item
