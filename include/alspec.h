@@ -341,22 +341,21 @@ typedef struct {
  * layers).  Each layer's outputs equal those of alspec_spec_decode (any
  * mode) on its inputs, bit for bit.
  *
- * p->overlap == 0 (default; 2 is taken as 0), one launch: a small kernel
- * first writes the table of the layers' buffers into the first layer's
- * workspace; then one launch runs the whole chain, its blocks taking work
- * items, one each, from a queue in that workspace: the first layer's sink
- * and window splits, then for each layer j in turn the merge of layer j's sink and
- * window states into its approximate output, layer j+1's sink and window
- * splits, layer j's middle splits and layer j-1's exact merge, verify and
- * commit, and last the last layer's verify.  A block takes the next item
- * when it starts, so faster compute units take more items, one layer's
- * slowest blocks do not delay the next layer's, and the launch's tail is
- * paid once per call.  Items that need others' results wait on per-layer
- * completion counts, and a layer's splits wait for the verify of the
- * latest earlier layer on the same workspace; every wait is bounded (one
- * that runs out leaves that layer's outputs wrong and counts itself in
- * the workspace; it does not hang).  Chains longer than 256 layers take
- * one such pair of launches per 256 layers.
+ * p->overlap == 0 (default; 2 is taken as 0), one launch: a small kernel first
+ * writes the table of the layers' buffers into the first layer's workspace;
+ * then one launch runs the whole chain, its blocks taking work items, one
+ * each, from a queue in that workspace: the first layer's sink and window
+ * splits, then for each layer j in turn the merge of layer j's sink and window
+ * states into its approximate output, layer j+1's sink and window splits,
+ * layer j's middle splits and layer j-1's exact merge, verify and commit, and
+ * last the last layer's verify.  A block takes the next item when it starts,
+ * so faster compute units take more items, one layer's slowest blocks do not
+ * delay the next layer's, and the launch's tail is paid once per call.  Items
+ * that need others' results wait on per-layer completion counts, and a layer's
+ * splits wait for the verify of the latest earlier layer on the same
+ * workspace; every wait is bounded (one that runs out leaves that layer's
+ * outputs wrong and counts itself in the workspace; it does not hang).  Chains
+ * longer than 256 layers take one such pair of launches per 256 layers.
  *
  * p->overlap == 1, one launch per layer: launch j computes, in disjoint
  * block ranges of one grid, the merge of layer j's sink and window states
