@@ -396,11 +396,11 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 // steps (q preparation, one tile, the split's end).
 template <int G>
 struct MfmaShared {
-  float p[kWaves][4][4][G];  // [wave][c][j][head]
+  float p[kWaves][4][4][G];  // [wave][c][j][head] (LDS form of P*V)
   float m[kWaves][G];
   float l[kWaves][G];
   float acc[kWaves][G][128];
-  bf16x8 q[3][4][64];
+  bf16x8 q[3][4][64];        // split q (LDS form)
 };
 
 template <int G>
@@ -553,8 +553,9 @@ struct MfmaWave {
     for (int i = 0; i < 8; ++i) qv[i] = qr[i];
   }
 
-  // The scaled q split into its three bf16 parts, per slice, in registers:
-  // the same operand values prepare_q stores in LDS.
+  // The scaled q (sm_scale log2(e); padding columns r >= G zeroed) split
+  // into its three bf16 parts, per slice, in registers: the B operands of
+  // the logits' MFMAs.
   __device__ __forceinline__ void split_q_regs(const float4 (&qv)[8],
                                                float sm_log2,
                                                bf16x8 (&qp)[3][4]) const {
@@ -568,10 +569,10 @@ struct MfmaWave {
     }
   }
 
-  // tile() with the split q in registers and the probabilities passed
-  // between lanes by row broadcasts: no LDS round trip inside the tile, for
-  // blocks that run alone on their CU, where nothing hides its latency.
-  // The same arithmetic in the same order as tile(), so the same bits.
+  // One 16-token tile of this wave (rows from tb, range end t1): logits on
+  // MFMA from the split q in registers, online softmax, P*V on the VALU
+  // with the probabilities passed between lanes by row broadcasts: no LDS
+  // round trip inside the tile.
   __device__ __forceinline__ void tile_regs(int tb, int t1,
                                             const u32x4 (&kr)[4],
                                             const u32x4 (&vr)[4],
@@ -680,14 +681,16 @@ struct MfmaWave {
 // [t0, t1), bf16 K/V with D = 128.  The logit block S^T = K_tile Q^T of a
 // 16-token tile is one 16x16 output of v_mfma_f32_16x16x32_bf16 per
 // 32-wide slice of D (K rows are the A operand straight from HBM, the
-// query heads the B operand, padded to 16 columns, kept in LDS).  q is
+// query heads the B operand, padded to 16 columns, in registers for G = 4
+// and in LDS for G = 8).  q is
 // split into three bf16 parts whose products accumulate in fp32, so the
 // logits keep fp32 accuracy.  Lane l (r = l % 16, c = l / 16) loads bytes
 // [64c, 64c + 64) of tile row r, and both operands map slice s, element j
 // to d = 32c + 8s + j.  The output gives lane l the logits of tokens
 // 4c + j (j = 0..3) for head r.  P*V runs on the VALU: lane l owns
-// d = 8r..8r+7 of V rows 4c + j and reads the G probabilities of its rows
-// from LDS.  Wave w takes tile w of every 64-token step of the range and
+// d = 8r..8r+7 of V rows 4c + j and takes the G probabilities of its rows
+// from the lanes of its row (row broadcasts for G = 4, LDS for G = 8).
+// Wave w takes tile w of every 64-token step of the range and
 // keeps NS register sets for K and V in turn: the loads of the next NS - 1
 // tiles are in flight while one is computed, and no set is copied into
 // another, so a wait covers only the loads of the tile about to be used.
@@ -709,32 +712,50 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
   const int last = t1 - 1;
   const int ta0 = t0 + wv.wave * TILE;  // this wave's tile i is at ta0 + i*STEP
 
-  // Each wave's q slice is requested first and the first NS - 1 tiles
-  // after it, so each wave's wait for its q slice leaves the tiles in
-  // flight.  Rows past the range are clamped to its last row.  (A loop-free
-  // form for splits of two steps, meant to request both tiles at once,
-  // measured slower: the compiler placed its tile loads behind the wait for
-  // q, and it cost 12 VGPRs.)
+  // q is requested first and the first NS - 1 tiles after it, so the wait
+  // for q leaves the tiles in flight.  For G = 4 each wave keeps all of q's
+  // three bf16 parts in registers and passes the probabilities from lane to
+  // lane by row broadcasts (tile_regs), so no tile waits on LDS (0.7 %
+  // faster at the 8B shape).  For G = 8 that form needs 188 VGPRs and ran
+  // 12 % slower at the 70B shape, so there each wave splits one 32-wide
+  // slice of q into LDS and the probabilities go through LDS (tile); both
+  // forms give the same bits.  Rows past the range are clamped to its last
+  // row.
+  constexpr bool kRegs = G == 4;
   u32x4 kr[NS][4], vr[NS][4];
-  float4 qv[2];
-  wv.load_q(qg, qv);
+  float4 qv[kRegs ? 8 : 2];
+  if constexpr (kRegs)
+    wv.load_q_full(qg, qv);
+  else
+    wv.load_q(qg, qv);
   if (t0 < t1) {
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
       wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
   }
-  wv.prepare_q(qv, sm_log2, sh);
-  __syncthreads();
+  bf16x8 qp[3][4];
+  if constexpr (kRegs) {
+    wv.split_q_regs(qv, sm_log2, qp);
+  } else {
+    wv.prepare_q(qv, sm_log2, sh);
+    __syncthreads();
+  }
+  auto tile = [&](int ta, const u32x4 (&k)[4], const u32x4 (&v)[4]) {
+    if constexpr (kRegs)
+      wv.tile_regs(ta, t1, k, v, qp);
+    else
+      wv.tile(ta, t1, k, v, sh);
+  };
 
   if constexpr (NS == 2) {
-    // spelled out: the compiler keeps this form in 18 fewer VGPRs
+    // spelled out: the compiler keeps this form in fewer VGPRs
     for (int blk = t0; blk < t1; blk += 2 * STEP) {
       const int ta = blk + wv.wave * TILE;
       wv.load(kb, vb, ta + STEP, last, kr[1], vr[1]);
-      wv.tile(ta, t1, kr[0], vr[0], sh);
+      tile(ta, kr[0], vr[0]);
       if (blk + STEP >= t1) break;
       wv.load(kb, vb, ta + 2 * STEP, last, kr[0], vr[0]);
-      wv.tile(ta + STEP, t1, kr[1], vr[1], sh);
+      tile(ta + STEP, kr[1], vr[1]);
     }
   } else {
     for (int blk = t0; blk < t1; blk += NS * STEP) {
@@ -743,7 +764,7 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
       for (int i = 0; i < NS; ++i) {
         wv.load(kb, vb, ta + (i + NS - 1) * STEP, last, kr[(i + NS - 1) % NS],
                 vr[(i + NS - 1) % NS]);
-        wv.tile(ta + i * STEP, t1, kr[i], vr[i], sh);
+        tile(ta + i * STEP, kr[i], vr[i]);
         if (i + 1 < NS && blk + (i + 1) * STEP >= t1) break;
       }
     }
@@ -751,13 +772,11 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
   wv.template finish<CO>(sh, out_ml, out_acc);
 }
 
-// split_state_mfma for a range of at most NT 64-token steps, for blocks
-// that run alone on their CU (the one-launch approximation): each wave
-// requests all of q and its NT tiles at once, keeps the split q in
-// registers and exchanges probabilities by row broadcasts, so the split
-// costs one memory round trip and no LDS round trip per tile.  The same
-// tiles, arithmetic and order as split_state_mfma, so the same bits.  The
-// range must be nonempty (every split of the plan is).
+// split_state_mfma for a range of at most NT 64-token steps (the sink and
+// window splits): each wave requests q and all its NT tiles at once, so the
+// split costs one memory round trip.  The same tiles, arithmetic and order
+// as split_state_mfma, so the same bits.  The range must be nonempty
+// (every split of the plan is).
 template <int G, int NT, bool CO>
 __device__ __forceinline__ void split_state_mfma_short(const float *__restrict__ qg,
                                        const uint16_t *__restrict__ kb,
