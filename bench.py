@@ -679,9 +679,39 @@ def main():
             if key in out:
                 out[key]["frac_of_probe_read"] = (
                     out[key]["achieved"] / pr["read"]["GBps"])
+        if "model_step" in out:
+            out["model_step"]["post_attention_roofline"][
+                "probe_at_size"] = post_probe_at_size(
+                    out["model_step"]["post_attention_roofline"])
+        log("probe done")
 
     print(json.dumps(out), flush=True)
     h.close()
+
+
+def post_probe_at_size(roof):
+    """The read probe at the byte count of each post-attention product (one
+    launch per product, back to back over distinct slices), and the layer
+    time those four probe launches take together: the ceiling that launch
+    ramps and tails leave for four short HBM-bound launches."""
+    from synth import device as sdev
+    from synth import post_gen as pg
+    ps = pg.llama8b(B=1)
+    sh = ps.shapes()
+    prod = {"o_proj": [sh["w_o"]], "gate_up": [sh["w_gate"], sh["w_up"]],
+            "down": [sh["w_down"]], "next_qkv": [sh["w_qkv"]]}
+    nbytes = {k: sum(r * c * 2 for r, c in v) for k, v in prod.items()}
+    pr = sdev.probe_read_sizes(sorted(set(nbytes.values())))
+    res = {}
+    for k, nb in nbytes.items():
+        r = pr[nb]
+        res[k] = {"bytes": nb, "us": r["us"], "GBps": r["GBps"],
+                  "settings": {x: r[x] for x in ("blocks", "loads_in_flight",
+                                                 "nontemporal")}}
+    probe_us = sum(r["us"] for r in res.values())
+    res["layer_probe_us"] = probe_us
+    res["layer_frac_of_probe"] = probe_us / roof["us_per_layer"]
+    return res
 
 
 def overhead_reduction(t_exact, t_approx, hit):

@@ -151,3 +151,56 @@ def probe_bandwidth(nbytes=4 << 30, reps=10, blocks=256 * 16):
            "copy": timed(copy, 2 * nbytes)}
     del src, dst, sink
     return res
+
+
+def probe_read_sizes(sizes, blocks=(256, 512, 1024, 2048), reps=None,
+                     pool_bytes=2 << 30):
+    """Achievable read bandwidth (GB/s) for single launches of given sizes:
+    for each size in `sizes` (bytes, multiples of 16), the fastest read-probe
+    setting over `blocks` x loads in flight x plain/nontemporal, each
+    setting timed with HIP events over back-to-back launches that walk
+    distinct slices of a `pool_bytes` buffer (well above the 256 MB of
+    last-level cache, so no launch re-reads cached bytes).  A short launch
+    pays its ramp and tail as a kernel of the same size does, so the result
+    is the ceiling such a kernel can be held to."""
+    import torch
+    lib = _probe_lib()
+    src = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(max(blocks), dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    base = src.data_ptr()
+    out = {}
+    for nb_ in sizes:
+        if nb_ % 16 or nb_ > pool_bytes:
+            raise ValueError(f"probe size {nb_} not usable")
+        slices = pool_bytes // nb_
+        n = reps or max(32, slices)
+
+        def launch(i, nb, u, nt):
+            rc = lib.probe_read(base + (i % slices) * nb_, nb_,
+                                sink.data_ptr(), nb, u, nt, s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe_read failed: {rc}")
+        best = None
+        for nb in blocks:
+            for u in PROBE_READ_UNROLL:
+                for nt in (0, 1):
+                    for i in range(4):
+                        launch(i, nb, u, nt)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(s)
+                    for i in range(n):
+                        launch(i, nb, u, nt)
+                    e1.record(s)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / n
+                    r = {"bytes": nb_, "us": us,
+                         "GBps": nb_ / (us * 1e-6) / 1e9, "blocks": nb,
+                         "loads_in_flight": u, "nontemporal": bool(nt)}
+                    if best is None or r["GBps"] > best["GBps"]:
+                        best = r
+        out[nb_] = best
+    del src, sink
+    return out

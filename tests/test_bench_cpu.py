@@ -72,3 +72,29 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_post_probe_at_size_products(monkeypatch):
+    """The probe is asked for each post-attention product's weight bytes
+    (Llama-3-8B layer, bf16) and its four launch times add up to the layer
+    ceiling, set against the measured layer time."""
+    from synth import device as sdev
+    asked = []
+
+    def fake(sizes):
+        asked.extend(sizes)
+        # 5000 GB/s at every size: t = bytes / 5e9 us
+        return {n: {"us": n / 5e3 / 1e3, "GBps": 5000.0, "blocks": 512,
+                    "loads_in_flight": 2, "nontemporal": True}
+                for n in sizes}
+    monkeypatch.setattr(sdev, "probe_read_sizes", fake)
+    res = bench.post_probe_at_size({"us_per_layer": 100.0})
+    want = {"o_proj": 4096 * 4096 * 2, "gate_up": 2 * 14336 * 4096 * 2,
+            "down": 4096 * 14336 * 2, "next_qkv": 6144 * 4096 * 2}
+    assert sorted(asked) == sorted(want.values())
+    for k, nb in want.items():
+        assert res[k]["bytes"] == nb
+        assert res[k]["us"] == pytest.approx(nb / 5e6)
+    total = sum(want.values()) / 5e6
+    assert res["layer_probe_us"] == pytest.approx(total)
+    assert res["layer_frac_of_probe"] == pytest.approx(total / 100.0)
