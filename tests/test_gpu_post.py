@@ -71,6 +71,9 @@ SHAPES = [
     ("b2_ragged", 2, 40, 48, 136, 20),
     ("b1_k_tail", 1, 520, 1032, 2056, 77),
     ("b2_long_k", 2, 256, 264, 14344, 9),
+    # one entry: the staged row form at its largest K (next QKV, K = 4096)
+    # beside the plain form just past it (output projection, K = 4104)
+    ("b1_stage_edges", 1, 4104, 4096, 136, 20),
     ("k_tail", 2, 520, 1032, 2056, 77),
     ("max_batch", 8, 256, 512, 1024, 384),
     ("mid_70b_like", 4, 1024, 2048, 5632, 3072),
