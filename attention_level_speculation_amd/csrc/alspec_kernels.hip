@@ -399,8 +399,16 @@ struct MfmaShared {
   float p[kWaves][4][4][G];  // [wave][c][j][head] (LDS form of P*V)
   float m[kWaves][G];
   float l[kWaves][G];
-  float acc[kWaves][G][128];
-  bf16x8 q[3][4][64];        // split q (LDS form)
+  union {
+    struct {
+      float acc[kWaves][G][128];
+      bf16x8 q[3][4][64];    // split q (LDS form)
+    };
+    // per wave, one K tile on its way into the MFMA operand layout (short
+    // splits with q in registers, which leave q unused; acc is written only
+    // after every wave's last tile)
+    uint4 kt[kWaves][256];
+  };
 };
 
 template <int G>
@@ -453,6 +461,48 @@ struct MfmaWave {
       vv[j] = __builtin_nontemporal_load(
           (const u32x4 *)(vb + (size_t)vrow * D + 8 * r));
     }
+  }
+
+  // The same tile with K loaded as V is: instruction i brings whole rows
+  // 4i .. 4i + 3 (lane l: row 4i + l / 16, bytes 16 (l % 16) ..), so both
+  // are loaded nontemporal; transpose_k then rearranges K for the MFMA.
+  __device__ __forceinline__ void load_rows(const uint16_t *__restrict__ kb,
+                                            const uint16_t *__restrict__ vb,
+                                            int tb, int last, u32x4 (&kk)[4],
+                                            u32x4 (&vv)[4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int krow = min(tb + 4 * i + c, last);
+      kk[i] = __builtin_nontemporal_load(
+          (const u32x4 *)(kb + (size_t)krow * D + 8 * r));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vrow = min(tb + 4 * c + j, last);
+      vv[j] = __builtin_nontemporal_load(
+          (const u32x4 *)(vb + (size_t)vrow * D + 8 * r));
+    }
+  }
+
+  // K of load_rows into the MFMA operand layout of load() through this
+  // wave's LDS buffer: row t, 16-byte piece j is stored at 16 t + (j ^ t),
+  // so that neither the stores (one row per 16 lanes) nor the loads (one
+  // piece of 16 rows per 16 lanes) meet in a bank.  LDS operations of one
+  // wave complete in order, so no wait separates the stores, the loads and
+  // the next tile's stores.
+  __device__ __forceinline__ void transpose_k(const u32x4 (&kr)[4],
+                                              u32x4 (&kx)[4],
+                                              uint4 *buf) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + c;
+      buf[row * 16 + (r ^ row)] = __builtin_bit_cast(uint4, kr[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kx[s] = __builtin_bit_cast(u32x4, buf[r * 16 + ((4 * c + s) ^ r)]);
+    __builtin_amdgcn_wave_barrier();
   }
 
   // q of head r, D slice s = wave (each of the four waves takes one 32-wide
@@ -803,11 +853,16 @@ __device__ __forceinline__ void split_state_mfma_short(const float *__restrict__
   u32x4 kr[NT][4], vr[NT][4];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
-    wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
+    wv.load_rows(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
   bf16x8 qp[3][4];
   wv.split_q_regs(qv, sm_log2, qp);
 #pragma unroll
-  for (int i = 0; i < NT; ++i) wv.tile_regs(ta0 + i * STEP, t1, kr[i], vr[i], qp);
+  for (int i = 0; i < NT; ++i) {
+    u32x4 kx[4];
+    wv.transpose_k(kr[i], kx, sh.kt[wv.wave]);
+    wv.tile_regs(ta0 + i * STEP, t1, kx, vr[i], qp);
+  }
+  __syncthreads();  // the K buffers share LDS with finish's acc
   wv.template finish<CO>(sh, out_ml, out_acc);
 }
 
