@@ -444,9 +444,11 @@ struct MfmaWave {
   // Unconditional loads keep the memory pipeline free of branches.
   // Every load instruction for V covers four whole rows, so V is loaded
   // nontemporal (read once): the middle pass went from 88.1 to 84.3 us at
-  // 128K, the same bits.  A K instruction covers 16-byte pieces of 16 rows
-  // (the MFMA operand layout), the rest of each line coming from the
-  // wave's next three instructions; nontemporal K loads were far slower.
+  // 128K, the same bits.  Here a K instruction covers 16-byte pieces of 16
+  // rows (the MFMA operand layout), the rest of each line coming from the
+  // wave's next three instructions, and nontemporal K loads were far
+  // slower; load_rows brings K in whole rows as well (nontemporal), for
+  // transpose_k to rearrange.
   __device__ __forceinline__ void load(const uint16_t *__restrict__ kb,
                                        const uint16_t *__restrict__ vb, int tb,
                                        int last, u32x4 (&kk)[4],
@@ -736,13 +738,13 @@ struct MfmaWave {
 // Softmax state of the G (4 or 8) query heads of one kv head over tokens
 // [t0, t1), bf16 K/V with D = 128.  The logit block S^T = K_tile Q^T of a
 // 16-token tile is one 16x16 output of v_mfma_f32_16x16x32_bf16 per
-// 32-wide slice of D (K rows are the A operand straight from HBM, the
-// query heads the B operand, padded to 16 columns, in registers for G = 4
-// and in LDS for G = 8).  q is
-// split into three bf16 parts whose products accumulate in fp32, so the
-// logits keep fp32 accuracy.  Lane l (r = l % 16, c = l / 16) loads bytes
-// [64c, 64c + 64) of tile row r, and both operands map slice s, element j
-// to d = 32c + 8s + j.  The output gives lane l the logits of tokens
+// 32-wide slice of D (K rows are the A operand, the query heads the B
+// operand, padded to 16 columns, in registers for G = 4 and in LDS for
+// G = 8).  q is split into three bf16 parts whose products accumulate in
+// fp32, so the logits keep fp32 accuracy.  In the A operand lane l
+// (r = l % 16, c = l / 16) holds bytes [64c, 64c + 64) of tile row r
+// (loaded so for G = 8, moved there through LDS for G = 4), and both
+// operands map slice s, element j to d = 32c + 8s + j.  The output gives lane l the logits of tokens
 // 4c + j (j = 0..3) for head r.  P*V runs on the VALU: lane l owns
 // d = 8r..8r+7 of V rows 4c + j and takes the G probabilities of its rows
 // from the lanes of its row (row broadcasts for G = 4, LDS for G = 8).
@@ -775,8 +777,10 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
   // faster at the 8B shape).  For G = 8 that form needs 188 VGPRs and ran
   // 12 % slower at the 70B shape, so there each wave splits one 32-wide
   // slice of q into LDS and the probabilities go through LDS (tile); both
-  // forms give the same bits.  Rows past the range are clamped to its last
-  // row.
+  // forms give the same bits.  The register form also loads K in whole
+  // rows, nontemporal, and transposes it through LDS (the middle pass at
+  // 128K: 84.1 against 87.5 us; 170 VGPRs, occupancy 2, against 152 and
+  // 3).  Rows past the range are clamped to its last row.
   constexpr bool kRegs = G == 4;
   u32x4 kr[NS][4], vr[NS][4];
   float4 qv[kRegs ? 8 : 2];
@@ -784,10 +788,15 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
     wv.load_q_full(qg, qv);
   else
     wv.load_q(qg, qv);
+  auto load = [&](int ta, u32x4 (&k)[4], u32x4 (&v)[4]) {
+    if constexpr (kRegs)
+      wv.load_rows(kb, vb, ta, last, k, v);
+    else
+      wv.load(kb, vb, ta, last, k, v);
+  };
   if (t0 < t1) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      wv.load(kb, vb, ta0 + i * STEP, last, kr[i], vr[i]);
+    for (int i = 0; i < NS - 1; ++i) load(ta0 + i * STEP, kr[i], vr[i]);
   }
   bf16x8 qp[3][4];
   if constexpr (kRegs) {
@@ -797,20 +806,23 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
     __syncthreads();
   }
   auto tile = [&](int ta, const u32x4 (&k)[4], const u32x4 (&v)[4]) {
-    if constexpr (kRegs)
-      wv.tile_regs(ta, t1, k, v, qp);
-    else
+    if constexpr (kRegs) {
+      u32x4 kx[4];
+      wv.transpose_k(k, kx, sh.kt[wv.wave]);
+      wv.tile_regs(ta, t1, kx, v, qp);
+    } else {
       wv.tile(ta, t1, k, v, sh);
+    }
   };
 
   if constexpr (NS == 2) {
     // spelled out: the compiler keeps this form in fewer VGPRs
     for (int blk = t0; blk < t1; blk += 2 * STEP) {
       const int ta = blk + wv.wave * TILE;
-      wv.load(kb, vb, ta + STEP, last, kr[1], vr[1]);
+      load(ta + STEP, kr[1], vr[1]);
       tile(ta, kr[0], vr[0]);
       if (blk + STEP >= t1) break;
-      wv.load(kb, vb, ta + 2 * STEP, last, kr[0], vr[0]);
+      load(ta + 2 * STEP, kr[0], vr[0]);
       tile(ta + STEP, kr[1], vr[1]);
     }
   } else {
@@ -818,13 +830,14 @@ __device__ __forceinline__ void split_state_mfma(const float *__restrict__ qg,
       const int ta = blk + wv.wave * TILE;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        wv.load(kb, vb, ta + (i + NS - 1) * STEP, last, kr[(i + NS - 1) % NS],
-                vr[(i + NS - 1) % NS]);
+        load(ta + (i + NS - 1) * STEP, kr[(i + NS - 1) % NS],
+             vr[(i + NS - 1) % NS]);
         tile(ta + i * STEP, kr[i], vr[i]);
         if (i + 1 < NS && blk + (i + 1) * STEP >= t1) break;
       }
     }
   }
+  if constexpr (kRegs) __syncthreads();  // K buffers share LDS with acc
   wv.template finish<CO>(sh, out_ml, out_acc);
 }
 
