@@ -89,20 +89,20 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "c3a6c066aea3a215e76e841a2f4aa3a5"
-                     "114d321d9022dde32cfbd8c06502b094",
+           "sha256": "3035c9f6944906cd11fa0a23e78faf73"
+                     "2d77db9d900eaebb4f7cb18be4702386",
            # (fetch, write) per launch: the per-layer chain kernel in its
            # steady state (all four block ranges), the exact split-K pass,
            # the one-launch chain of the 32 layers at 128K, and the two
            # chain forms of the 32K configuration
-           "bytes": {"chain": (262908.1 * 1024 * 2.0, 862.4 * 1024 * 1.0),
-                     "partials_middle": (258175.5 * 1024 * 2.0,
+           "bytes": {"chain": (262897.1 * 1024 * 2.0, 862.8 * 1024 * 1.0),
+                     "partials_middle": (258181.5 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0),
-                     "one_chain": (8408203.2 * 1024 * 2.0,
-                                   30020.0 * 1024 * 1.0),
-                     "c2_one_chain": (2115439.2 * 1024 * 2.0,
-                                      29452.1 * 1024 * 1.0),
-                     "c2_chain": (66289.7 * 1024 * 2.0, 846.3 * 1024 * 1.0)}}
+                     "one_chain": (8405509.5 * 1024 * 2.0,
+                                   30015.7 * 1024 * 1.0),
+                     "c2_one_chain": (2114783.3 * 1024 * 2.0,
+                                      29449.3 * 1024 * 1.0),
+                     "c2_chain": (66296.7 * 1024 * 2.0, 846.3 * 1024 * 1.0)}}
 
 
 def measured_traffic(kernel):
