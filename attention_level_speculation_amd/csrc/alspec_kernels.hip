@@ -1387,9 +1387,8 @@ template <class KV, int D, int G>
 __device__ __forceinline__ void approx_fused_body(
     const PlanArgs &pa, const Item &it, const float *__restrict__ q,
     const typename KV::elem *__restrict__ k,
-    const typename KV::elem *__restrict__ v, int L_cap, float sm_log2,
-    const WsPtrs &w, const Outs &o) {
-  const int Hq = pa.Hq;
+    const typename KV::elem *__restrict__ v, int L_cap, int Hq,
+    float sm_log2, const WsPtrs &w, const Outs &o) {
   const size_t kv_off = ((size_t)it.b * pa.Hkv + it.g) * L_cap * D;
   const int h0 = it.g * G;
   split_any<KV, D, G, true, true>(q + ((size_t)it.b * Hq + h0) * D,
@@ -1409,18 +1408,23 @@ __global__ __launch_bounds__(kThreads) void approx_fused_kernel(
     const typename KV::elem *__restrict__ v, float sm_log2, WsPtrs w,
     Outs o) {
   const Item it = decode_item(pa, true, blockIdx.x);
-  approx_fused_body<KV, D, G>(pa, it, q, k, v, pa.L_cap, sm_log2, w, o);
+  approx_fused_body<KV, D, G>(pa, it, q, k, v, pa.L_cap, pa.Hq, sm_log2, w,
+                              o);
 }
 
 // The same for a launch over batch entry 0 alone.  The leading scalar
-// arguments are all the first memory requests depend on (the item's kv
-// head and token range, the cache stride and the q, K and V bases); the
-// library is built to preload the leading kernel arguments into scalar
-// registers at wave launch, so those requests leave without waiting for a
-// kernel-argument fetch.
+// arguments are all that the first memory requests and the addresses
+// computed before them depend on (the item's kv head and token range, the
+// cache stride, the head count of the state slots and the q, K and V
+// bases: 14 dwords, as many as the hardware preloads); the library is built
+// to preload the leading kernel arguments into scalar registers at wave
+// launch, so those requests leave without waiting for a kernel-argument
+// fetch (with the head count read from the plan they waited for one, which
+// measured within noise of this form).  The plan has a sink split exactly
+// when the sink is nonempty.
 template <class KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void approx_fused_one_kernel(
-    int n_split, int nsink, int s_end, int w_begin, int Tw, int L, int L_cap,
+    int n_split, int s_end, int w_begin, int Tw, int L, int L_cap, int Hq,
     const float *__restrict__ q, const typename KV::elem *__restrict__ k,
     const typename KV::elem *__restrict__ v, PlanArgs pa, float sm_log2,
     WsPtrs w, Outs o) {
@@ -1429,6 +1433,7 @@ __global__ __launch_bounds__(kThreads) void approx_fused_one_kernel(
   it.g = blockIdx.x / n_split;
   const int a = blockIdx.x - it.g * n_split;
   it.slot = a;  // entry 0's slots start at 0
+  const int nsink = s_end > 0 ? 1 : 0;
   if (a < nsink) {
     it.t0 = 0;
     it.t1 = s_end;
@@ -1436,7 +1441,7 @@ __global__ __launch_bounds__(kThreads) void approx_fused_one_kernel(
     it.t0 = w_begin + (a - nsink) * Tw;
     it.t1 = min(L, it.t0 + Tw);
   }
-  approx_fused_body<KV, D, G>(pa, it, q, k, v, L_cap, sm_log2, w, o);
+  approx_fused_body<KV, D, G>(pa, it, q, k, v, L_cap, Hq, sm_log2, w, o);
 }
 
 // Merge of one head group's sink and window states (one block per
@@ -1907,8 +1912,8 @@ hipError_t approx_fused_kg(const PlanArgs &pa, const float *q, const void *k,
   using E = typename KV::elem;
   if (pa.B == 1)
     return launch(approx_fused_one_kernel<KV, D, G>, dim3(items),
-                  dim3(kThreads), s, pa.nsink[0] + pa.nwin[0], pa.nsink[0],
-                  pa.s_end[0], pa.w_begin[0], pa.Tw, pa.L[0], pa.L_cap, q,
+                  dim3(kThreads), s, pa.nsink[0] + pa.nwin[0], pa.s_end[0],
+                  pa.w_begin[0], pa.Tw, pa.L[0], pa.L_cap, pa.Hq, q,
                   (const E *)k, (const E *)v, pa, sm_log2, w, o);
   return launch(approx_fused_kernel<KV, D, G>, dim3(items), dim3(kThreads), s,
                 pa, q, (const E *)k, (const E *)v, sm_log2, w, o);
