@@ -89,20 +89,20 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "3035c9f6944906cd11fa0a23e78faf73"
-                     "2d77db9d900eaebb4f7cb18be4702386",
+           "sha256": "8e7b56396ef9a286c011a88a677d6b0c"
+                     "f4bba73fcd0879ea458ed28129f98a2d",
            # (fetch, write) per launch: the per-layer chain kernel in its
            # steady state (all four block ranges), the exact split-K pass,
            # the one-launch chain of the 32 layers at 128K, and the two
            # chain forms of the 32K configuration
-           "bytes": {"chain": (262897.1 * 1024 * 2.0, 862.8 * 1024 * 1.0),
-                     "partials_middle": (258181.5 * 1024 * 2.0,
+           "bytes": {"chain": (262897.1 * 1024 * 2.0, 862.6 * 1024 * 1.0),
+                     "partials_middle": (258181.6 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0),
-                     "one_chain": (8405509.5 * 1024 * 2.0,
+                     "one_chain": (8405514.0 * 1024 * 2.0,
                                    30015.7 * 1024 * 1.0),
-                     "c2_one_chain": (2114783.3 * 1024 * 2.0,
-                                      29449.3 * 1024 * 1.0),
-                     "c2_chain": (66296.7 * 1024 * 2.0, 846.3 * 1024 * 1.0)}}
+                     "c2_one_chain": (2114816.7 * 1024 * 2.0,
+                                      29449.2 * 1024 * 1.0),
+                     "c2_chain": (66297.3 * 1024 * 2.0, 846.3 * 1024 * 1.0)}}
 
 
 def measured_traffic(kernel):
@@ -899,11 +899,29 @@ def B_params_seq(al, p):
     return q
 
 
+# The model step's residual stream: one coordinate far above the others
+# (sets the query's planted part through the next QKV's RMSNorm).
+MASSIVE_DIM = 1234
+MASSIVE_VALUE = 2.0e3
+
+
 def model_timing(args, al, h, w, Q, K, V, nl, dev):
     """One decode token through nl Llama-3-8B-shaped layers: the attention
     step on the resident 128K KV, then the post-attention operators with
     seeded random bf16 weights (o_proj, RMSNorm + gated MLP, down, RMSNorm
     + next QKV; 416 MiB per layer), layer l+1's query from layer l's QKV.
+
+    The weights carry the structure that makes a trained model's queries
+    find the sink: the residual stream holds one dominant coordinate
+    (MASSIVE_DIM, MASSIVE_VALUE), so after the RMSNorm of the next QKV that
+    coordinate is close to sqrt(hidden) whatever the rest holds; that
+    norm's weight is 1 there, and the QKV weight's column there gives query
+    head h of kv head g the entries a * u_g / sqrt(hidden), u_g being the
+    planted direction of the next layer's KV cache (the generator's
+    queries carry a * u_g in the same way).  The random rest of each query
+    plays the part of the generator's query noise.  Without it the queries
+    are unrelated to the planted sink and needles, and no layer commits.
+
     Timed by wall clock between synchronisations, in four forms:
       exact_only      exact attention, then post-attention on its output
       spec_sequence   attention step with verify, then post-attention on
@@ -925,6 +943,7 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
     import torch
 
     from attention_level_speculation_amd import runtime as rt
+    from synth import gen
     from synth import post_gen as pg
     ps = pg.llama8b(B=1)
     pp = al.make_post_params(1, ps.attn_dim, ps.hidden, ps.ffn, ps.qkv_dim,
@@ -940,12 +959,24 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
             else:
                 t = torch.randn(shp, device=dev, generator=gen_)
                 t *= shp[1] ** -0.5
+            if n_ == "norm_attn":
+                t[MASSIVE_DIM] = 1.0
+            if n_ == "w_qkv":
+                # query rows: the next layer's planted directions
+                nxt = (layer + 1) % nl
+                for g in range(w.Hkv):
+                    u = torch.from_numpy(gen.head_plant(w, nxt, 0, g).u).to(
+                        device=dev, dtype=torch.float32)
+                    col = w.const.a * u / ps.hidden ** 0.5
+                    for hq in range(g * w.G, (g + 1) * w.G):
+                        t[hq * w.D:(hq + 1) * w.D, MASSIVE_DIM] = col
             d[n_] = t.to(torch.bfloat16)
         weights.append(d)
     structs = [al.post_weights_struct(pp, d) for d in weights]
     f = dict(dtype=torch.float32, device=dev)
     hs = [torch.randn((1, ps.hidden), generator=gen_, **f)] + [
         torch.empty((1, ps.hidden), **f) for _ in range(nl)]
+    hs[0][0, MASSIVE_DIM] = MASSIVE_VALUE
     qkvs = [torch.empty((1, ps.qkv_dim), **f) for _ in range(nl)]
     wsp = (al.alloc_post_workspace(pp, dev), al.alloc_post_workspace(pp, dev))
     sa, se = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
@@ -953,7 +984,9 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
     res = {"workload": "llama3-8b-shaped decoder layers, batch 1: attention "
                        "over the 128K bf16 KV of one density (4 needles), "
                        "then post-attention with seeded random bf16 "
-                       "weights", "layers": nl,
+                       "weights whose next-QKV query rows point at the "
+                       "next layer's planted sink direction through one "
+                       "dominant residual coordinate", "layers": nl,
            "post_weight_bytes_per_layer": ps.weight_bytes(),
            "steps": args.model_steps}
 
