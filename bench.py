@@ -94,7 +94,8 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
            # (fetch, write) per launch: the per-layer chain kernel in its
            # steady state (all four block ranges), the exact split-K pass,
            # the one-launch chain of the 32 layers at 128K, and the two
-           # chain forms of the 32K configuration
+           # chain forms of the 32K, multi-user and 70B configurations
+           # (the one-launch chain over all of their layers)
            "bytes": {"chain": (262897.1 * 1024 * 2.0, 862.6 * 1024 * 1.0),
                      "partials_middle": (258181.6 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0),
@@ -102,7 +103,15 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                                    30015.7 * 1024 * 1.0),
                      "c2_one_chain": (2114816.7 * 1024 * 2.0,
                                       29449.2 * 1024 * 1.0),
-                     "c2_chain": (66297.3 * 1024 * 2.0, 846.3 * 1024 * 1.0)}}
+                     "c2_chain": (66297.3 * 1024 * 2.0, 846.3 * 1024 * 1.0),
+                     "c4_one_chain": (51413770.2 * 1024 * 2.0,
+                                      48896.4 * 1024 * 1.0),
+                     "c4_chain": (1607014.8 * 1024 * 2.0,
+                                  1432.5 * 1024 * 1.0),
+                     "c5_one_chain": (84012888.9 * 1024 * 2.0,
+                                      186949.6 * 1024 * 1.0),
+                     "c5_chain": (1050756.8 * 1024 * 2.0,
+                                  2213.1 * 1024 * 1.0)}}
 
 
 def measured_traffic(kernel):
