@@ -908,12 +908,6 @@ def B_params_seq(al, p):
     return q
 
 
-# The model step's residual stream: one coordinate far above the others
-# (sets the query's planted part through the next QKV's RMSNorm).
-MASSIVE_DIM = 1234
-MASSIVE_VALUE = 2.0e3
-
-
 def model_timing(args, al, h, w, Q, K, V, nl, dev):
     """One decode token through nl Llama-3-8B-shaped layers: the attention
     step on the resident 128K KV, then the post-attention operators with
@@ -921,10 +915,11 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
     + next QKV; 416 MiB per layer), layer l+1's query from layer l's QKV.
 
     The weights carry the structure that makes a trained model's queries
-    find the sink: the residual stream holds one dominant coordinate
-    (MASSIVE_DIM, MASSIVE_VALUE), so after the RMSNorm of the next QKV that
-    coordinate is close to sqrt(hidden) whatever the rest holds; that
-    norm's weight is 1 there, and the QKV weight's column there gives query
+    find the sink (post_gen.plant_query_direction): the residual stream
+    holds one dominant coordinate (post_gen.MASSIVE_DIM, MASSIVE_VALUE), so
+    after the RMSNorm of the next QKV that coordinate is close to
+    sqrt(hidden) whatever the rest holds; that norm's weight is 1 there,
+    and the QKV weight's column there gives query
     head h of kv head g the entries a * u_g / sqrt(hidden), u_g being the
     planted direction of the next layer's KV cache (the generator's
     queries carry a * u_g in the same way).  The random rest of each query
@@ -968,24 +963,19 @@ def model_timing(args, al, h, w, Q, K, V, nl, dev):
             else:
                 t = torch.randn(shp, device=dev, generator=gen_)
                 t *= shp[1] ** -0.5
-            if n_ == "norm_attn":
-                t[MASSIVE_DIM] = 1.0
-            if n_ == "w_qkv":
-                # query rows: the next layer's planted directions
-                nxt = (layer + 1) % nl
-                for g in range(w.Hkv):
-                    u = torch.from_numpy(gen.head_plant(w, nxt, 0, g).u).to(
-                        device=dev, dtype=torch.float32)
-                    col = w.const.a * u / ps.hidden ** 0.5
-                    for hq in range(g * w.G, (g + 1) * w.G):
-                        t[hq * w.D:(hq + 1) * w.D, MASSIVE_DIM] = col
-            d[n_] = t.to(torch.bfloat16)
-        weights.append(d)
+            d[n_] = t
+        # query rows: the next layer's planted directions
+        nxt = (layer + 1) % nl
+        pg.plant_query_direction(
+            d["w_qkv"], d["norm_attn"],
+            [gen.head_plant(w, nxt, 0, g).u for g in range(w.Hkv)],
+            w.const.a, w.D, w.G, ps.hidden)
+        weights.append({n_: t.to(torch.bfloat16) for n_, t in d.items()})
     structs = [al.post_weights_struct(pp, d) for d in weights]
     f = dict(dtype=torch.float32, device=dev)
     hs = [torch.randn((1, ps.hidden), generator=gen_, **f)] + [
         torch.empty((1, ps.hidden), **f) for _ in range(nl)]
-    hs[0][0, MASSIVE_DIM] = MASSIVE_VALUE
+    hs[0][0, pg.MASSIVE_DIM] = pg.MASSIVE_VALUE
     qkvs = [torch.empty((1, ps.qkv_dim), **f) for _ in range(nl)]
     wsp = (al.alloc_post_workspace(pp, dev), al.alloc_post_workspace(pp, dev))
     sa, se = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)

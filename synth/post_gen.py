@@ -73,3 +73,34 @@ def activations(s: PostShape, step: int = 0):
     o = rng.standard_normal((s.B, s.attn_dim), dtype=np.float32)
     h = rng.standard_normal((s.B, s.hidden), dtype=np.float32)
     return o, h
+
+
+# The chained decode step's residual stream: one coordinate far above the
+# others, through which the next QKV's query rows are pointed at the next
+# layer's planted sink direction (plant_query_direction).
+MASSIVE_DIM = 1234
+MASSIVE_VALUE = 2.0e3
+
+
+def plant_query_direction(w_qkv, norm_attn, dirs, a, D, G, hidden,
+                          dim=MASSIVE_DIM):
+    """Make the query rows of a QKV weight point at planted directions.
+
+    w_qkv: float tensor [qkv_dim][hidden] (query rows first, head-major),
+    norm_attn: float tensor [hidden], both modified in place (torch tensors
+    on any device, before rounding to bf16); dirs: one unit vector of D
+    floats per kv head; a: the planted query component.  With a residual
+    stream whose coordinate `dim` is far above the others, RMSNorm maps that
+    coordinate to about sqrt(hidden) whatever the rest holds; the norm's
+    weight is set to 1 there and the column `dim` of query head h (kv head
+    h // G) to a * dirs[h // G] / sqrt(hidden), so the query carries
+    a * dirs[g] plus the random product of the other coordinates, as the
+    generator's queries carry a * u."""
+    import torch
+    norm_attn[dim] = 1.0
+    scale = a / float(hidden) ** 0.5
+    for g, u in enumerate(dirs):
+        col = torch.as_tensor(u, dtype=torch.float32).to(w_qkv.device) * scale
+        for hq in range(g * G, (g + 1) * G):
+            w_qkv[hq * D:(hq + 1) * D, dim] = col
+
