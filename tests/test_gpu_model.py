@@ -18,6 +18,11 @@ work and replay on discard (attention_level_speculation_amd.runtime).
   sequence's result, matches the oracle chain where the flags are not in
   doubt, and, captured into one HIP graph, replays to the eager result
   bit for bit, three times with eager work in between.
+- With planted weights (each next query pointed at the next layer's
+  planted sink direction, synth.post_gen.plant_query_direction) the later
+  layers' queries find the sink as the generator's do, and at lambda 0.05
+  the flags go commit, commit, discard: both forms give the committed
+  sequence's bits and the oracle chain's flags and outputs.
 - A captured graph of the two-stream speculative step replaying to the
   eager result is skipped: capture crashed the host inside the HIP runtime
   (see the test's reason).
@@ -48,19 +53,38 @@ def handle():
     h.close()
 
 
-def _setup(lam, kv="f32"):
+PLANT_DIM = 7   # the residual's dominant coordinate at hidden 256
+
+
+def _setup(lam, kv="f32", planted=False):
     Hq, Hkv, D, L = 8, 2, 64, 3000
     w = gen.Workload("model", B=1, Hq=Hq, Hkv=Hkv, D=D, L_cap=L,
                      seq_lens=[L], kv_dtype=kv, S=4, W=128, lam=lam,
-                     needles=[1], seed=31)
+                     needles=[0 if planted else 1], seed=31)
     ps = pg.PostShape("model", 1, Hq * D, 256, 512, (Hq + 2 * Hkv) * D,
                       seed=32)
+    weights = [pg.weights(pg.PostShape(ps.name, ps.B, ps.attn_dim,
+                                       ps.hidden, ps.ffn, ps.qkv_dim,
+                                       ps.eps, ps.seed + l))
+               for l in range(N_LAYERS)]
+    h0 = pg.activations(ps)[1]
+    if planted:
+        for l, wt in enumerate(weights):
+            # planted in float, rounded once to bf16 (the other entries
+            # are bf16 values already, so rounding again keeps them)
+            wq = torch.from_numpy(gen.bf16_bits_to_f32(wt["w_qkv"]).copy())
+            na = torch.from_numpy(
+                gen.bf16_bits_to_f32(wt["norm_attn"]).copy())
+            nxt = (l + 1) % N_LAYERS
+            pg.plant_query_direction(
+                wq, na, [gen.head_plant(w, nxt, 0, g).u for g in range(Hkv)],
+                w.const.a, D, Hq // Hkv, ps.hidden, dim=PLANT_DIM)
+            wt["w_qkv"] = gen.f32_to_bf16_bits(wq.numpy())
+            wt["norm_attn"] = gen.f32_to_bf16_bits(na.numpy())
+        h0 = h0.copy()
+        h0[0, PLANT_DIM] = pg.MASSIVE_VALUE
     host = {"kv": [gen.layer_inputs(w, l) for l in range(N_LAYERS)],
-            "w": [pg.weights(pg.PostShape(ps.name, ps.B, ps.attn_dim,
-                                          ps.hidden, ps.ffn, ps.qkv_dim,
-                                          ps.eps, ps.seed + l))
-                  for l in range(N_LAYERS)],
-            "h0": pg.activations(ps)[1]}
+            "w": weights, "h0": h0}
     return w, ps, host
 
 
@@ -141,13 +165,15 @@ def test_one_stream_equals_committed_sequence(handle, lam):
     assert np.array_equal(hs, hq) and np.array_equal(qs, qq)
 
 
-def _oracle_chain(w, ps, host, lam):
+def _oracle_chain(w, ps, host, lam, ratios=None):
     q = host["kv"][0][0].astype(np.float64)
     h = host["h0"].astype(np.float64)
     for l in range(N_LAYERS):
         _, k, v = host["kv"][l]
         r = oracle.spec_decode(q.astype(np.float32), k, v, w.seq_lens, w.S,
                                w.W, lam)
+        if ratios is not None:
+            ratios.append(float(r["ratio"][0]))
         o = r["o_committed"].reshape(1, -1)
         h, qkv = op.post_attention(o, h, host["w"][l], ps.eps)
         q = qkv[:, :ps.attn_dim].reshape(1, w.Hq, w.D)
@@ -178,6 +204,28 @@ def test_one_stream_matches_oracle_chain(handle, lam):
     print(f"[case] one-stream chain vs oracle lam={lam}: h {eh:.2e} "
           f"qkv {eq:.2e}", flush=True)
     assert eh <= 1e-4 and eq <= 1e-4
+
+
+@pytest.mark.parametrize("one_stream", [False, True])
+def test_planted_queries_mix_commits(handle, one_stream):
+    lam = 0.05
+    w, ps, host = _setup(lam, planted=True)
+    ratios = []
+    ho, qo = _oracle_chain(w, ps, host, lam, ratios)
+    want = [int(r <= lam) for r in ratios]
+    # the flags are not in doubt, and they mix
+    assert min(abs(r - lam) for r in ratios) > 1e-4, ratios
+    assert want == [1, 1, 0], ratios
+    dev = _device(w, ps, host, lam)
+    print(f"[case] planted model one_stream={one_stream}", flush=True)
+    hs, qs, flags = _run(handle, dev, speculative=True, one_stream=one_stream)
+    hq, qq, flags2 = _run(handle, dev, speculative=False)
+    print(f"[case] commits {flags}, oracle ratios {ratios}", flush=True)
+    assert flags == flags2 == want
+    assert np.array_equal(hs, hq) and np.array_equal(qs, qq)
+    eh = np.linalg.norm(hs - ho) / np.linalg.norm(ho)
+    eq = np.linalg.norm(qs - qo) / np.linalg.norm(qo)
+    assert eh <= 1e-4 and eq <= 1e-4, (eh, eq)
 
 
 def test_one_stream_graph_replays_match_eager(handle):
