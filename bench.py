@@ -89,29 +89,28 @@ TRAFFIC = {"sources": ("attention_level_speculation_amd/csrc/alspec_kernels.hip"
                        "attention_level_speculation_amd/csrc/alspec_kernels.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.h",
                        "attention_level_speculation_amd/csrc/alspec_plan.cpp"),
-           "sha256": "8e7b56396ef9a286c011a88a677d6b0c"
-                     "f4bba73fcd0879ea458ed28129f98a2d",
+           "sha256": "ec93685d7c6304dd62558aef1d105358"
+                     "0b1d6958527130677d5bc31f7a993072",
            # (fetch, write) per launch: the per-layer chain kernel in its
            # steady state (all four block ranges), the exact split-K pass,
            # the one-launch chain of the 32 layers at 128K, and the two
            # chain forms of the 32K, multi-user and 70B configurations
            # (the one-launch chain over all of their layers)
-           "bytes": {"chain": (262897.1 * 1024 * 2.0, 862.6 * 1024 * 1.0),
-                     "partials_middle": (258181.6 * 1024 * 2.0,
+           "bytes": {"chain": (262912.0 * 1024 * 2.0, 862.6 * 1024 * 1.0),
+                     "partials_middle": (258181.1 * 1024 * 2.0,
                                          520.0 * 1024 * 1.0),
-                     "one_chain": (8405514.0 * 1024 * 2.0,
-                                   30015.7 * 1024 * 1.0),
-                     "c2_one_chain": (2114816.7 * 1024 * 2.0,
-                                      29449.2 * 1024 * 1.0),
-                     "c2_chain": (66297.3 * 1024 * 2.0, 846.3 * 1024 * 1.0),
-                     "c4_one_chain": (51413770.2 * 1024 * 2.0,
-                                      48896.4 * 1024 * 1.0),
-                     "c4_chain": (1607014.8 * 1024 * 2.0,
-                                  1432.5 * 1024 * 1.0),
-                     "c5_one_chain": (84012888.9 * 1024 * 2.0,
-                                      186949.6 * 1024 * 1.0),
-                     "c5_chain": (1050756.8 * 1024 * 2.0,
-                                  2213.1 * 1024 * 1.0)}}
+                     "one_chain": (8405447.9 * 1024 * 2.0,
+                                   30015.5 * 1024 * 1.0),
+                     "c2_one_chain": (2114859.2 * 1024 * 2.0,
+                                      29449.3 * 1024 * 1.0),
+                     "c2_chain": (66303.8 * 1024 * 2.0, 846.6 * 1024 * 1.0),
+                     "c4_one_chain": (51413771.4 * 1024 * 2.0,
+                                      48896.1 * 1024 * 1.0),
+                     "c4_chain": (1607038.4 * 1024 * 2.0, 1432.5 * 1024 * 1.0),
+                     "c5_one_chain": (84013249.6 * 1024 * 2.0,
+                                      186951.1 * 1024 * 1.0),
+                     "c5_chain": (1050750.6 * 1024 * 2.0,
+                                  2213.7 * 1024 * 1.0)}}
 
 
 def measured_traffic(kernel):

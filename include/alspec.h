@@ -358,10 +358,11 @@ typedef struct {
  * longer than 256 layers take one such pair of launches per 256 layers.
  *
  * p->overlap == 1, one launch per layer: launch j computes, in disjoint
- * block ranges of one grid, the merge of layer j's sink and window states
- * (for j >= 1; dispatched first), layer j's middle splits, layer j+1's sink
- * and window splits, and layer j-1's exact merge, verify and commit; a last
- * launch verifies layer n-1.  Stream order alone carries the dependencies.
+ * block ranges of one grid, layer j's middle splits (dispatched first),
+ * layer j+1's sink and window splits, the merge of layer j's sink and
+ * window states (for j >= 1), and layer j-1's exact merge, verify and
+ * commit; a last launch verifies layer n-1.  Stream order alone carries
+ * the dependencies.
  *
  * A stack whose next query is computed from the approximate output runs
  * through the single-layer calls instead.  `layers` is a host array of
