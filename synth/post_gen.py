@@ -6,7 +6,8 @@ operators' arithmetic.
 Weights are N(0, 1/fan_in) rounded to bf16 (so each product keeps unit
 scale); the RMSNorm weights are 1 + 0.1 N(0, 1).  Activations are N(0, 1)
 fp32.  Everything comes from one numpy Generator seeded with `seed`, in a
-fixed order.
+fixed order.  For a chain of layers, plant_query_direction points each
+next query at the next layer's planted sink direction (see there).
 """
 from dataclasses import dataclass
 
@@ -103,4 +104,3 @@ def plant_query_direction(w_qkv, norm_attn, dirs, a, D, G, hidden,
         col = torch.as_tensor(u, dtype=torch.float32).to(w_qkv.device) * scale
         for hq in range(g * G, (g + 1) * G):
             w_qkv[hq * D:(hq + 1) * D, dim] = col
-
