@@ -621,10 +621,23 @@ def main():
                         "includes the layer-table writer before it)")
             else:
                 achieved = layer_bytes / (lus * 1e-6) / 1e9
-                kern = ("chain_kernel<KvBf16,128,4> (steady state: merge of "
-                        "layer j's approximation, middle splits of layer j, "
-                        "sink and window splits of layer j+1, verify of "
-                        "layer j-1)")
+                kern = ("chain_kernel<KvBf16,128,4> (steady state: middle "
+                        "splits of layer j, dispatched first, sink and "
+                        "window splits of layer j+1, merge of layer j's "
+                        "approximation, verify of layer j-1)")
+                # when the approximate output is there: every block of the
+                # launch is resident from its start, so layer j's merge
+                # ends a few microseconds into launch j, and its verdict
+                # and committed output a few into launch j+1
+                res[best]["approximate_output"] = {
+                    "ready": "layer j's approximate output is merged by "
+                             "blocks of launch j that start with it (its "
+                             "sink and window splits ran in launch j-1); "
+                             "its exact output, verdict and committed "
+                             "output come from blocks of launch j+1",
+                    "lead_over_committed_output_us": lus,
+                    "lead_measure": "one steady launch (HIP events, as "
+                                    "roofline.launch_us_mean)"}
             out["roofline"] = {
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
